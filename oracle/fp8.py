@@ -43,9 +43,28 @@ def round_to_grid(x, mant_bits, emin):
     return np.copysign(r, x)
 
 
+CHUNK = 1 << 20
+
+
+def _chunked(fn, x, out_dtype):
+    """Apply an elementwise function over a flattened array in cache-sized
+    pieces (numpy is much slower on large multi-dimensional temporaries)."""
+    x = np.asarray(x)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, out_dtype)
+    for i in range(0, flat.size, CHUNK):
+        out[i:i + CHUNK] = fn(flat[i:i + CHUNK])
+    return out.reshape(x.shape)
+
+
 def e4m3_decode(codes):
-    """Decode uint8 E4M3 codes to float64 (NaN for S.1111.111)."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    """Decode uint8 E4M3 codes to float64 (NaN for S.1111.111): a lookup in the
+    256-entry table that the bit-field decoder below produces."""
+    return _DECODE_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def _e4m3_decode(codes):
+    c = codes.astype(np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = c & 0x7
@@ -54,6 +73,9 @@ def e4m3_decode(codes):
     v = np.where(e == 0, sub, nrm)
     v = np.where((e == 15) & (m == 7), np.nan, v)
     return sign * v
+
+
+_DECODE_TABLE = _e4m3_decode(np.arange(256, dtype=np.uint8))
 
 
 def e4m3_round(x):
@@ -66,6 +88,10 @@ def e4m3_encode(x):
     """Encode values as E4M3 codes: RNE to the grid, saturate, then pack the
     sign, exponent and mantissa fields.  -0 and values rounding to zero from
     below keep the sign bit (code 0x80)."""
+    return _chunked(_e4m3_encode, x, np.uint8)
+
+
+def _e4m3_encode(x):
     x = np.asarray(x, dtype=np.float64)
     v = e4m3_round(x)
     av = np.abs(v)

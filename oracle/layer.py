@@ -86,7 +86,7 @@ def moe_layer(x, wg, bias, experts, n_groups, topk_groups, k, route_scale):
     rows = T * k + T
     f = None
     y = np.zeros((rows, d), np.float32)
-    hq = hs = None
+    hq = hs = g = u = h = None
     for e in range(E + 1):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
@@ -96,15 +96,17 @@ def moe_layer(x, wg, bias, experts, n_groups, topk_groups, k, route_scale):
             f = w13q.shape[0] // 2
             hq = np.zeros((rows, f), np.uint8)
             hs = np.zeros((rows, f // 128), np.float32)
+            g, u, h = (np.zeros((rows, f), np.float32) for _ in range(3))
         ye, inter = expert_ffn(xq_perm[lo:hi], xs_perm[lo:hi], w13q, w13s, w2q, w2s)
         y[lo:hi] = ye
         hq[lo:hi] = inter["hq"]
         hs[lo:hi] = inter["hs"]
+        g[lo:hi], u[lo:hi], h[lo:hi] = inter["g"], inter["u"], inter["h"]
     y_routed = y[np.asarray(pos, np.int64)]                   # [T, k, d]
     out = combine(y_routed, r["w"], y[T * k:T * k + T])
     return {"route": r, "xq": xq, "xs": xs, "offsets": offsets, "pos": pos,
             "row_token": row_token, "xq_perm": xq_perm, "xs_perm": xs_perm,
-            "hq": hq, "hs": hs, "y": y, "out": out}
+            "g": g, "u": u, "h": h, "hq": hq, "hs": hs, "y": y, "out": out}
 
 
 def moe_layer_tokens(x_rows, wg, bias, experts, n_groups, topk_groups, k, route_scale):
@@ -112,7 +114,9 @@ def moe_layer_tokens(x_rows, wg, bias, experts, n_groups, topk_groups, k, route_
     routing acts on one token at a time (1x128 tiles lie within a row, experts act
     row-wise, the combine is per token) and routing is per token, so this equals
     the corresponding rows of the whole-batch layer.  Returns (out [n, d],
-    route dict)."""
+    route dict, intermediates: y_routed [n, k, d], y_shared [n, d], and the
+    expert_ffn intermediates per (token, slot) and per token for the shared
+    expert)."""
     x_rows = np.asarray(x_rows, np.float32)
     n, d = x_rows.shape
     E = np.asarray(wg).shape[0]
@@ -121,15 +125,21 @@ def moe_layer_tokens(x_rows, wg, bias, experts, n_groups, topk_groups, k, route_
     y_routed = np.zeros((n, k, d), np.float32)
     y_shared = np.zeros((n, d), np.float32)
     need = {}
+    inter_routed, inter_shared = {}, {}
     for t in range(n):
         for j in range(k):
             need.setdefault(int(r["idx"][t, j]), []).append((t, j))
     for e in sorted(need):
         w13q, w13s, w2q, w2s = experts(e)
         ts = [t for t, _ in need[e]]
-        ye, _ = expert_ffn(xq[ts], xs[ts], w13q, w13s, w2q, w2s)
-        for (t, j), row in zip(need[e], ye):
+        ye, inter = expert_ffn(xq[ts], xs[ts], w13q, w13s, w2q, w2s)
+        for i, ((t, j), row) in enumerate(zip(need[e], ye)):
             y_routed[t, j] = row
+            inter_routed[(t, j)] = {key: val[i:i + 1] for key, val in inter.items()}
     w13q, w13s, w2q, w2s = experts(E)
-    y_shared[:], _ = expert_ffn(xq, xs, w13q, w13s, w2q, w2s)
-    return combine(y_routed, r["w"], y_shared), r
+    y_shared[:], inter = expert_ffn(xq, xs, w13q, w13s, w2q, w2s)
+    for t in range(n):
+        inter_shared[t] = {key: val[t:t + 1] for key, val in inter.items()}
+    extra = {"xq": xq, "xs": xs, "y_routed": y_routed, "y_shared": y_shared,
+             "inter_routed": inter_routed, "inter_shared": inter_shared}
+    return combine(y_routed, r["w"], y_shared), r, extra

@@ -1,1 +1,192 @@
-"""MI355X (gfx950) forward pass of a DeepSeek-V3 MoE layer."""
+"""Forward pass of one DeepSeek-V3 MoE layer on an MI355X (gfx950).
+
+The compute lives in libmoe.so (hand-written HIP kernels behind a C ABI, see
+``include/moe.h``).  This module is the thin Python binding: each function
+has the name of a C entry point, takes torch tensors that already live on the
+GPU, and passes their pointers plus the current HIP stream.  PyTorch provides
+device memory and streams only.  ``MoELayer`` strings the six calls together
+with preallocated buffers.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import MoEError, RouteParams  # noqa: F401
+
+__all__ = ["moe_route", "fp8_quant_1x128", "fp8_quant_128x128", "moe_permute_workspace_bytes",
+           "moe_permute", "grouped_gemm_fp8_swiglu", "moe_combine", "MoEWeights", "MoELayer",
+           "MoEError", "RouteParams"]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def moe_route(x, wg, bias, n_groups, topk_groups, topk, route_scale, idx, w, stream=None):
+    """Router: idx [T, k] int32 (ascending expert ids), w [T, k] float32."""
+    _dev(x, torch.bfloat16, "x"); _dev(wg, torch.bfloat16, "wg"); _dev(bias, torch.float32, "bias")
+    _dev(idx, torch.int32, "idx"); _dev(w, torch.float32, "w")
+    T, d = x.shape
+    p = RouteParams(wg.shape[0], n_groups, topk_groups, topk, route_scale)
+    lib = _lib.load()
+    _lib.check("moe_route", lib.moe_route(_ptr(x), _ptr(wg), _ptr(bias), T, d, p, _ptr(idx), _ptr(w),
+                                          _stream(stream)))
+
+
+def fp8_quant_1x128(x, q, scale, stream=None):
+    """x [rows, cols] BF16 -> q [rows, cols] uint8 E4M3, scale [rows, cols/128] float32."""
+    _dev(x, torch.bfloat16, "x"); _dev(q, torch.uint8, "q"); _dev(scale, torch.float32, "scale")
+    rows, cols = x.shape
+    lib = _lib.load()
+    _lib.check("fp8_quant_1x128", lib.fp8_quant_1x128(_ptr(x), rows, cols, _ptr(q), _ptr(scale),
+                                                      _stream(stream)))
+
+
+def fp8_quant_128x128(w, q, scale, stream=None):
+    """w [..., N, K] BF16 (leading dims folded into N) -> q uint8, scale [..., N/128, K/128]."""
+    _dev(w, torch.bfloat16, "w"); _dev(q, torch.uint8, "q"); _dev(scale, torch.float32, "scale")
+    K = w.shape[-1]
+    N = w.numel() // K
+    lib = _lib.load()
+    _lib.check("fp8_quant_128x128", lib.fp8_quant_128x128(_ptr(w), N, K, _ptr(q), _ptr(scale),
+                                                          _stream(stream)))
+
+
+def moe_permute_workspace_bytes(T, k, E):
+    return int(_lib.load().moe_permute_workspace_bytes(T, k, E))
+
+
+def moe_permute(idx, n_experts, offsets, pos, row_token, workspace, xq=None, xs=None,
+                xq_perm=None, xs_perm=None, stream=None):
+    """Group assignments by expert: offsets [E+2], pos [T, k], row_token [T*k + T];
+    optionally copies the FP8 rows into xq_perm / xs_perm."""
+    for t, dt, n in ((idx, torch.int32, "idx"), (offsets, torch.int32, "offsets"),
+                     (pos, torch.int32, "pos"), (row_token, torch.int32, "row_token"),
+                     (workspace, torch.uint8, "workspace"), (xq, torch.uint8, "xq"),
+                     (xs, torch.float32, "xs"), (xq_perm, torch.uint8, "xq_perm"),
+                     (xs_perm, torch.float32, "xs_perm")):
+        _dev(t, dt, n)
+    T, k = idx.shape
+    d = xq.shape[1] if xq is not None else 0
+    lib = _lib.load()
+    _lib.check("moe_permute", lib.moe_permute(
+        _ptr(idx), T, k, n_experts, _ptr(xq), _ptr(xs), d, _ptr(offsets), _ptr(pos),
+        _ptr(row_token), _ptr(xq_perm), _ptr(xs_perm), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
+
+
+def grouped_gemm_fp8_swiglu(aq, as_, row_src, offsets, w13, w13_s, w2, w2_s, h, hs, y, stream=None):
+    """Both expert GEMMs: h/hs [rows, f] E4M3 + scales, y [rows, d] BF16."""
+    for t, dt, n in ((aq, torch.uint8, "aq"), (as_, torch.float32, "as"),
+                     (row_src, torch.int32, "row_src"), (offsets, torch.int32, "offsets"),
+                     (w13, torch.uint8, "w13"), (w13_s, torch.float32, "w13_s"),
+                     (w2, torch.uint8, "w2"), (w2_s, torch.float32, "w2_s"),
+                     (h, torch.uint8, "h"), (hs, torch.float32, "hs"), (y, torch.bfloat16, "y")):
+        _dev(t, dt, n)
+    n_groups, two_f, d = w13.shape
+    rows = h.shape[0]
+    lib = _lib.load()
+    _lib.check("grouped_gemm_fp8_swiglu", lib.grouped_gemm_fp8_swiglu(
+        _ptr(aq), _ptr(as_), aq.shape[0], _ptr(row_src), _ptr(offsets), n_groups, rows, d,
+        two_f // 2, _ptr(w13), _ptr(w13_s), _ptr(w2), _ptr(w2_s), _ptr(h), _ptr(hs), _ptr(y),
+        _stream(stream)))
+
+
+def moe_combine(y, pos, w, shared_row0, out, stream=None):
+    """out [T, d] = BF16(sum_j w[t, j] * y[pos[t, j]] + y[shared_row0 + t])."""
+    _dev(y, torch.bfloat16, "y"); _dev(pos, torch.int32, "pos"); _dev(w, torch.float32, "w")
+    _dev(out, torch.bfloat16, "out")
+    T, k = pos.shape
+    lib = _lib.load()
+    _lib.check("moe_combine", lib.moe_combine(_ptr(y), _ptr(pos), _ptr(w), T, k, y.shape[1],
+                                              shared_row0, _ptr(out), _stream(stream)))
+
+
+class MoEWeights:
+    """FP8 expert weights of one layer: w13 [E+1, 2f, d], w2 [E+1, d, f] E4M3
+    with 128x128 block scales; index E is the shared expert."""
+
+    def __init__(self, w13q, w13s, w2q, w2s):
+        self.w13q, self.w13s, self.w2q, self.w2s = w13q, w13s, w2q, w2s
+        self.n_groups, two_f, self.d = w13q.shape
+        self.f = two_f // 2
+
+    @classmethod
+    def empty(cls, n_groups, d, f, device="cuda"):
+        return cls(torch.empty(n_groups, 2 * f, d, dtype=torch.uint8, device=device),
+                   torch.empty(n_groups, 2 * f // 128, d // 128, dtype=torch.float32, device=device),
+                   torch.empty(n_groups, d, f, dtype=torch.uint8, device=device),
+                   torch.empty(n_groups, d // 128, f // 128, dtype=torch.float32, device=device))
+
+    def quantize_expert(self, e, w13_bf16, w2_bf16, stream=None):
+        """Offline 128x128 quantisation of expert e's BF16 weights into place."""
+        fp8_quant_128x128(w13_bf16, self.w13q[e], self.w13s[e], stream)
+        fp8_quant_128x128(w2_bf16, self.w2q[e], self.w2s[e], stream)
+
+
+class MoELayer:
+    """Buffers and call sequence of the layer for up to ``T`` tokens:
+    moe_route -> fp8_quant_1x128 -> moe_permute -> grouped_gemm_fp8_swiglu -> moe_combine.
+
+    With ``dispatch=False`` (default) the permute produces only the metadata and
+    the first GEMM reads each token's FP8 row through row_token; with
+    ``dispatch=True`` the rows are first copied into grouped order."""
+
+    def __init__(self, T, d, E, n_groups, topk_groups, topk, f, route_scale=2.5, device="cuda",
+                 dispatch=False):
+        self.T, self.d, self.E, self.k, self.f = T, d, E, topk, f
+        self.n_groups, self.topk_groups, self.route_scale = n_groups, topk_groups, route_scale
+        self.dispatch = dispatch
+        rows = T * topk + T
+        dev = dict(device=device)
+        self.idx = torch.empty(T, topk, dtype=torch.int32, **dev)
+        self.w = torch.empty(T, topk, dtype=torch.float32, **dev)
+        self.xq = torch.empty(T, d, dtype=torch.uint8, **dev)
+        self.xs = torch.empty(T, d // 128, dtype=torch.float32, **dev)
+        self.offsets = torch.empty(E + 2, dtype=torch.int32, **dev)
+        self.pos = torch.empty(T, topk, dtype=torch.int32, **dev)
+        self.row_token = torch.empty(rows, dtype=torch.int32, **dev)
+        self.ws = torch.empty(max(16, moe_permute_workspace_bytes(T, topk, E)), dtype=torch.uint8, **dev)
+        self.xq_perm = torch.empty(rows, d, dtype=torch.uint8, **dev) if dispatch else None
+        self.xs_perm = torch.empty(rows, d // 128, dtype=torch.float32, **dev) if dispatch else None
+        self.h = torch.empty(rows, f, dtype=torch.uint8, **dev)
+        self.hs = torch.empty(rows, f // 128, dtype=torch.float32, **dev)
+        self.y = torch.empty(rows, d, dtype=torch.bfloat16, **dev)
+        self.out = torch.empty(T, d, dtype=torch.bfloat16, **dev)
+
+    def forward(self, x, wg, bias, weights, stream=None):
+        moe_route(x, wg, bias, self.n_groups, self.topk_groups, self.k, self.route_scale,
+                  self.idx, self.w, stream)
+        fp8_quant_1x128(x, self.xq, self.xs, stream)
+        if self.dispatch:
+            moe_permute(self.idx, self.E, self.offsets, self.pos, self.row_token, self.ws,
+                        self.xq, self.xs, self.xq_perm, self.xs_perm, stream)
+            grouped_gemm_fp8_swiglu(self.xq_perm, self.xs_perm, None, self.offsets, weights.w13q,
+                                    weights.w13s, weights.w2q, weights.w2s, self.h, self.hs, self.y,
+                                    stream)
+        else:
+            moe_permute(self.idx, self.E, self.offsets, self.pos, self.row_token, self.ws,
+                        stream=stream)
+            grouped_gemm_fp8_swiglu(self.xq, self.xs, self.row_token, self.offsets, weights.w13q,
+                                    weights.w13s, weights.w2q, weights.w2s, self.h, self.hs, self.y,
+                                    stream)
+        moe_combine(self.y, self.pos, self.w, self.T * self.k, self.out, stream)
+        return self.out

@@ -1,0 +1,230 @@
+// C ABI of libmoe: host-side validation, then launches on the caller's stream.
+// Validation is synchronous and touches no device memory; an invalid call
+// returns an error code before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define REQUIRE(cond, ...)                                 \
+  do {                                                     \
+    if (!(cond)) return fail(MOE_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+// Byte and BF16 matrices are accessed with 16-byte vector loads/stores; FP32
+// and int32 arrays element by element.
+#define REQUIRE_PTR_A(p, a)                                                   \
+  do {                                                                        \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #p);   \
+    if (!aligned((p), (a)))                                                   \
+      return fail(MOE_ERR_INVALID_ARG, "%s is not %d-byte aligned", #p, (int)(a)); \
+  } while (0)
+#define REQUIRE_PTR(p) REQUIRE_PTR_A(p, 16)
+#define REQUIRE_PTR4(p) REQUIRE_PTR_A(p, 4)
+
+#define REQUIRE_ALIGNED4_OR_NULL(p)                                           \
+  do {                                                                        \
+    if ((p) != nullptr && !aligned((p), 4))                                   \
+      return fail(MOE_ERR_INVALID_ARG, "%s is not 4-byte aligned", #p);       \
+  } while (0)
+
+moe_status check_route_params(const moe_route_params& p) {
+  REQUIRE(p.n_experts >= 1 && p.n_experts <= 256, "n_experts=%d must be in [1, 256]", p.n_experts);
+  REQUIRE(p.n_groups >= 1 && p.n_groups <= 64, "n_groups=%d must be in [1, 64]", p.n_groups);
+  REQUIRE(p.n_experts % p.n_groups == 0, "n_experts=%d is not a multiple of n_groups=%d",
+          p.n_experts, p.n_groups);
+  REQUIRE(p.topk_groups >= 1 && p.topk_groups <= p.n_groups, "topk_groups=%d must be in [1, %d]",
+          p.topk_groups, p.n_groups);
+  REQUIRE(p.topk >= 1, "topk=%d must be >= 1", p.topk);
+  REQUIRE(p.topk % p.topk_groups == 0, "topk=%d is not a multiple of topk_groups=%d", p.topk,
+          p.topk_groups);
+  const int per = p.n_experts / p.n_groups;
+  REQUIRE(p.topk / p.topk_groups <= per, "topk/topk_groups=%d exceeds the %d experts of a group",
+          p.topk / p.topk_groups, per);
+  REQUIRE(p.topk <= p.topk_groups * per, "topk=%d exceeds the %d experts of the kept groups",
+          p.topk, p.topk_groups * per);
+  REQUIRE(std::isfinite(p.route_scale), "route_scale is not finite");
+  if (p.topk > 16) return fail(MOE_ERR_UNSUPPORTED, "topk=%d > 16 is not implemented", p.topk);
+  if (p.topk / p.topk_groups > 8)
+    return fail(MOE_ERR_UNSUPPORTED, "topk/topk_groups=%d > 8 is not implemented",
+                p.topk / p.topk_groups);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status moe_route(const uint16_t* x, const uint16_t* wg, const float* bias, int T, int d,
+                     moe_route_params p, int32_t* idx, float* w, void* stream) {
+  clear_error();
+  REQUIRE(T >= 0, "T=%d is negative", T);
+  moe_status s = check_route_params(p);
+  if (s != MOE_OK) return s;
+  REQUIRE(d >= 128 && d % 128 == 0, "d=%d must be a positive multiple of 128", d);
+  if (T == 0) return MOE_OK;
+  REQUIRE(T <= INT32_MAX / p.topk, "T*k overflows int32");
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(wg);
+  REQUIRE_ALIGNED4_OR_NULL(bias);
+  REQUIRE_PTR4(idx);
+  REQUIRE_PTR4(w);
+  return hip_status(moe::launch_route(x, wg, bias, T, d, p.n_experts, p.n_groups, p.topk_groups,
+                                      p.topk, p.route_scale, idx, w,
+                                      static_cast<hipStream_t>(stream)),
+                    "moe_route launch");
+}
+
+moe_status fp8_quant_1x128(const uint16_t* x, int rows, int cols, uint8_t* q, float* scale,
+                           void* stream) {
+  clear_error();
+  REQUIRE(rows >= 0, "rows=%d is negative", rows);
+  REQUIRE(cols >= 128 && cols % 128 == 0, "cols=%d must be a positive multiple of 128", cols);
+  if (rows == 0) return MOE_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR4(scale);
+  return hip_status(moe::launch_quant_1x128(x, rows, cols, q, scale, static_cast<hipStream_t>(stream)),
+                    "fp8_quant_1x128 launch");
+}
+
+moe_status fp8_quant_128x128(const uint16_t* w, int N, int K, uint8_t* q, float* scale,
+                             void* stream) {
+  clear_error();
+  REQUIRE(N >= 0 && N % 128 == 0, "N=%d must be a non-negative multiple of 128", N);
+  REQUIRE(K >= 128 && K % 128 == 0, "K=%d must be a positive multiple of 128", K);
+  if (N == 0) return MOE_OK;
+  if (N / 128 > 65535) return fail(MOE_ERR_UNSUPPORTED, "N/128=%d exceeds 65535", N / 128);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR4(scale);
+  return hip_status(moe::launch_quant_128x128(w, N, K, q, scale, static_cast<hipStream_t>(stream)),
+                    "fp8_quant_128x128 launch");
+}
+
+size_t moe_permute_workspace_bytes(int T, int k, int E) {
+  (void)k;
+  if (T <= 0 || E <= 0) return 0;
+  return moe::permute_workspace_bytes(T, E);
+}
+
+moe_status moe_permute(const int32_t* idx, int T, int k, int E, const uint8_t* xq, const float* xs,
+                       int d, int32_t* offsets, int32_t* pos, int32_t* row_token, uint8_t* xq_perm,
+                       float* xs_perm, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  REQUIRE(T >= 0, "T=%d is negative", T);
+  REQUIRE(E >= 1 && E <= 256, "E=%d must be in [1, 256]", E);
+  REQUIRE(k >= 1 && k <= 16 && k <= E, "k=%d must be in [1, min(16, E)]", k);
+  if (T == 0) return MOE_OK;
+  REQUIRE(T <= INT32_MAX / (k + 1), "T*(k+1) overflows int32");
+  REQUIRE_PTR4(idx);
+  REQUIRE_PTR4(offsets);
+  REQUIRE_PTR4(pos);
+  REQUIRE_PTR4(row_token);
+  if (xq_perm != nullptr) {
+    REQUIRE(d >= 128 && d % 128 == 0, "d=%d must be a positive multiple of 128", d);
+    REQUIRE_PTR(xq);
+    REQUIRE_PTR4(xs);
+    REQUIRE_PTR(xq_perm);
+    REQUIRE_PTR4(xs_perm);
+  }
+  const size_t need = moe::permute_workspace_bytes(T, E);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  REQUIRE(aligned(workspace, 4), "workspace is not 4-byte aligned");
+  return hip_status(moe::launch_permute(idx, T, k, E, xq, xs, d, offsets, pos, row_token, xq_perm,
+                                        xs_perm, workspace, static_cast<hipStream_t>(stream)),
+                    "moe_permute launch");
+}
+
+moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, int a_rows,
+                                   const int32_t* row_src, const int32_t* offsets, int n_groups,
+                                   int total_rows, int d, int f, const uint8_t* w13,
+                                   const float* w13_s, const uint8_t* w2, const float* w2_s,
+                                   uint8_t* h, float* hs, uint16_t* y, void* stream) {
+  clear_error();
+  REQUIRE(n_groups >= 1, "n_groups=%d must be >= 1", n_groups);
+  if (n_groups > 1024) return fail(MOE_ERR_UNSUPPORTED, "n_groups=%d > 1024", n_groups);
+  REQUIRE(total_rows >= 0, "total_rows=%d is negative", total_rows);
+  REQUIRE(d >= 128 && d % 128 == 0, "d=%d must be a positive multiple of 128", d);
+  REQUIRE(f >= 128 && f % 128 == 0, "f=%d must be a positive multiple of 128", f);
+  if (total_rows == 0) return MOE_OK;
+  REQUIRE(a_rows >= 1, "a_rows=%d must be >= 1", a_rows);
+  REQUIRE(row_src != nullptr || a_rows >= total_rows,
+          "a_rows=%d < total_rows=%d without row_src", a_rows, total_rows);
+  REQUIRE_PTR(aq);
+  REQUIRE_PTR4(as);
+  REQUIRE_ALIGNED4_OR_NULL(row_src);
+  REQUIRE_PTR4(offsets);
+  REQUIRE_PTR(w13);
+  REQUIRE_PTR4(w13_s);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR4(w2_s);
+  REQUIRE_PTR(h);
+  REQUIRE_PTR4(hs);
+  REQUIRE_PTR(y);
+  return hip_status(moe::launch_grouped_gemm(aq, as, row_src, offsets, n_groups, total_rows, d, f,
+                                             w13, w13_s, w2, w2_s, h, hs, y,
+                                             static_cast<hipStream_t>(stream), a_rows),
+                    "grouped_gemm_fp8_swiglu launch");
+}
+
+moe_status moe_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k, int d,
+                       int32_t shared_row0, uint16_t* out, void* stream) {
+  clear_error();
+  REQUIRE(T >= 0, "T=%d is negative", T);
+  REQUIRE(k >= 1 && k <= 16, "k=%d must be in [1, 16]", k);
+  REQUIRE(d >= 128 && d % 128 == 0, "d=%d must be a positive multiple of 128", d);
+  REQUIRE(shared_row0 >= -1, "shared_row0=%d must be >= -1", shared_row0);
+  if (T == 0) return MOE_OK;
+  REQUIRE(T <= INT32_MAX / (k + 1), "T*(k+1) overflows int32");
+  REQUIRE_PTR(y);
+  REQUIRE_PTR4(pos);
+  REQUIRE_PTR4(w);
+  REQUIRE_PTR(out);
+  return hip_status(moe::launch_combine(y, pos, w, T, k, d, shared_row0, out,
+                                        static_cast<hipStream_t>(stream)),
+                    "moe_combine launch");
+}
+
+}  // extern "C"

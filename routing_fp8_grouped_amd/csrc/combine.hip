@@ -1,0 +1,72 @@
+// Combine: each token's routed expert outputs weighted by its gates, plus the
+// shared expert's output, in BF16 (the book's chapter 7 "Selecting and
+// combining experts": the routed weights sum to one and the shared expert is
+// added separately; chapter 15 "What combine must do": token identity is kept;
+// chapter 17 "FP8 dispatch, BF16 combine").
+//
+// One workgroup per token; each thread owns 8 consecutive columns (16-byte
+// loads of every source row, one 16-byte store).  The sum is FP32 in slot
+// order, then the shared row, so the result is deterministic.  HBM-bound:
+// (k + 1) BF16 rows read and one written per token.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ w, int k, int d,
+                                                      int rows, int shared_row0,
+                                                      uint16_t* __restrict__ out) {
+  __shared__ int s_pos[16];
+  __shared__ float s_w[16];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    const int p = pos[(size_t)t * k + threadIdx.x];
+    const bool ok = p >= 0 && p < rows;   // an unassigned slot contributes nothing
+    s_pos[threadIdx.x] = ok ? p : 0;
+    s_w[threadIdx.x] = ok ? w[(size_t)t * k + threadIdx.x] : 0.0f;
+  }
+  __syncthreads();
+  const int n8 = d / 8;
+  for (int c = threadIdx.x; c < n8; c += 256) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)s_pos[j] * d + c * 8);
+      const float wj = s_w[j];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu)), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i] >> 16)), acc[2 * i + 1]);
+      }
+    }
+    if (shared_row0 >= 0) {
+      const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)(shared_row0 + t) * d + c * 8);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
+        acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
+      }
+    }
+    uint4 o;
+    o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+    o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out + (size_t)t * d + c * 8) = o;
+  }
+}
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k,
+                          int d, int shared_row0, uint16_t* out, hipStream_t stream) {
+  const int rows = T * k + (shared_row0 >= 0 ? T : 0);
+  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, stream, y, pos, w, k, d,
+                     shared_row0 >= 0 ? shared_row0 + T : rows, shared_row0, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,73 @@
+// Device helpers shared by the gfx950 kernels of libmoe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even FP32 -> BF16 for finite values.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two FP32 values to two E4M3 codes (low byte = a).  The hardware conversion
+// rounds to nearest even and keeps subnormals; clamping first makes magnitudes
+// above 448 saturate instead of becoming NaN.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  a = fminf(fmaxf(a, -kE4M3Max), kE4M3Max);
+  b = fminf(fmaxf(b, -kE4M3Max), kE4M3Max);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Four FP32 values to four packed E4M3 codes (byte i = v_i).
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float v0, float v1, float v2, float v3) {
+  v0 = fminf(fmaxf(v0, -kE4M3Max), kE4M3Max);
+  v1 = fminf(fmaxf(v1, -kE4M3Max), kE4M3Max);
+  v2 = fminf(fmaxf(v2, -kE4M3Max), kE4M3Max);
+  v3 = fminf(fmaxf(v3, -kE4M3Max), kE4M3Max);
+  uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, r, true);
+}
+
+// Scale of a tile from its max-abs value: amax/448 (correctly rounded FP32
+// division), 1.0 for an all-zero tile.
+__device__ __forceinline__ float scale_from_amax(float amax) {
+  return amax == 0.0f ? 1.0f : amax / kE4M3Max;
+}
+
+// One 16x16x128 FP8 E4M3 MFMA: D = A * B^T + C.  Lane l supplies row l%16 of A
+// (and row l%16 of B, i.e. column l%16 of the product) with the 32 K-values
+// [(l/16)*32, (l/16)*32 + 32); D holds rows (l/16)*4 + i, column l%16.  The
+// E8M0 block scales are fixed at 2^0 (code 127).
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// 16x16x32 BF16 MFMA with the same row/column conventions; lane l holds the 8
+// K-values [(l/16)*8, (l/16)*8 + 8).
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,36 @@
+// Launch functions of the gfx950 kernels (host side of each .hip file).  Every
+// function enqueues on `stream` and returns hipGetLastError(); arguments are
+// validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_quant_1x128(const uint16_t* x, long rows, int cols, uint8_t* q, float* scale,
+                              hipStream_t stream);
+hipError_t launch_quant_128x128(const uint16_t* w, int N, int K, uint8_t* q, float* scale,
+                                hipStream_t stream);
+
+hipError_t launch_route(const uint16_t* x, const uint16_t* wg, const float* bias, int T, int d,
+                        int E, int G, int M, int k, float route_scale, int32_t* idx, float* w,
+                        hipStream_t stream);
+
+size_t permute_workspace_bytes(int T, int E);
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const uint8_t* xq,
+                          const float* xs, int d, int32_t* offsets, int32_t* pos,
+                          int32_t* row_token, uint8_t* xq_perm, float* xs_perm, void* ws,
+                          hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const uint8_t* aq, const float* as, const int32_t* row_src,
+                               const int32_t* offsets, int n_groups, int total_rows, int d, int f,
+                               const uint8_t* w13, const float* w13_s, const uint8_t* w2,
+                               const float* w2_s, uint8_t* h, float* hs, uint16_t* y,
+                               hipStream_t stream, int a_rows);
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k,
+                          int d, int shared_row0, uint16_t* out, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,249 @@
+"""Shared helpers of the GPU parity tests: device inputs, FP8 weights through the
+HIP path, and the oracle's view of the same seeded inputs."""
+
+import concurrent.futures as cf
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import routing_fp8_grouped_amd as moe
+from routing_fp8_grouped_amd import configs, inputs
+from oracle import layer as olayer
+
+DEV = "cuda"
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_np(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.float().numpy()
+    return t.numpy()
+
+
+def rel_l2_rows(a, b):
+    """Per-row relative L2 error of a against reference b."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    num = np.linalg.norm(a - b, axis=-1)
+    den = np.linalg.norm(b, axis=-1)
+    return num / np.maximum(den, 1e-30)
+
+
+def device_weights(cfg, bf16_cache=None):
+    """Generate every expert's BF16 weights on the GPU (seeded per expert) and
+    quantise them with the library's 128x128 kernel (the offline step)."""
+    W = moe.MoEWeights.empty(cfg.E + 1, cfg.d, cfg.f)
+    for e in range(cfg.E + 1):
+        w13, w2 = inputs.expert_weights(cfg, e, DEV)
+        W.quantize_expert(e, w13, w2)
+        if bf16_cache is not None:
+            bf16_cache[e] = (w13, w2)
+    torch.cuda.synchronize()
+    return W
+
+
+class OracleExperts:
+    """The oracle's quantised weights of the experts it needs, quantised by the
+    oracle from the same BF16 weights the GPU quantised (regenerated per expert
+    with the same seed, copied to the host)."""
+
+    def __init__(self, cfg, bf16_cache=None):
+        self.cfg = cfg
+        self.cache = {}
+        self.bf16 = bf16_cache
+
+    def _host(self, e):
+        if self.bf16 is not None and e in self.bf16:
+            w13, w2 = self.bf16[e]
+        else:
+            w13, w2 = inputs.expert_weights(self.cfg, e, DEV)
+        return w13.float().cpu().numpy(), w2.float().cpu().numpy()
+
+    def prepare(self, ids, workers=None):
+        ids = [int(e) for e in ids if int(e) not in self.cache]
+        if not ids:
+            return
+        host = {e: self._host(e) for e in ids}
+        workers = workers or min(16, os.cpu_count() or 4)
+        with cf.ThreadPoolExecutor(workers) as ex:
+            res = ex.map(lambda e: (e, olayer.quantize_expert(*host[e])), ids)
+            for e, q in res:
+                self.cache[e] = q
+
+    def __call__(self, e):
+        if int(e) not in self.cache:
+            self.prepare([e])
+        return self.cache[int(e)]
+
+
+def host_inputs(cfg):
+    x, wg, b = inputs.host_inputs(cfg)
+    return x, wg, b
+
+
+def run_layer(cfg, x, wg, b, W, dispatch=False):
+    L = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.f, cfg.route_scale,
+                     dispatch=dispatch)
+    L.forward(x.to(DEV), wg.to(DEV), b.to(DEV), W)
+    torch.cuda.synchronize()
+    return L
+
+
+# ---- codes of h with two valid values ------------------------------------------
+#
+# The GPU computes each 128-wide K block's partial sum with one E4M3 MFMA, which
+# sums its 128 products with an unbiased error of RMS 1.87e-6 and at most
+# 1.39e-5 of sum|a*b| (measured on gfx950 over 1M dot products of random
+# quantised tiles).  G and U, and
+# so h = SiLU(G) * U, therefore differ from the oracle's exact blocked sums by a
+# small, bounded amount, and an element of h that lies that close to an E4M3
+# rounding midpoint has two correct codes.  These helpers flag such elements
+# from oracle quantities alone and bound what a one-step code change can do to
+# the expert output, the way near-tie tokens are handled for routing.
+
+from oracle import fp8 as ofp8, quant as oquant
+
+MFMA_BLOCK_RMS = 1.87e-6   # RMS of (block sum - exact) / sum|a*b|
+MFMA_BLOCK_MAX = 1.39e-5   # largest observed |block sum - exact| / sum|a*b|
+
+
+def block_abs_sums(aq_rows, as_rows, wq, ws):
+    """Per output element, over the 128-wide K blocks kb of sa*sw*sum|a||w|:
+    returns (sqrt of the sum of squares, the largest one)."""
+    a = ofp8.e4m3_decode(np.asarray(aq_rows) & 0x7F)
+    w = ofp8.e4m3_decode(np.asarray(wq) & 0x7F)
+    sa = np.asarray(as_rows, np.float64)
+    sw = np.repeat(np.asarray(ws, np.float64), 128, axis=0)
+    ss = np.zeros((a.shape[0], w.shape[0]))
+    mx = np.zeros_like(ss)
+    for kb in range(a.shape[1] // 128):
+        blk = slice(kb * 128, (kb + 1) * 128)
+        p = (a[:, blk] @ w[:, blk].T) * sa[:, kb:kb + 1] * sw[None, :, kb]
+        ss += p * p
+        np.maximum(mx, p, out=mx)
+    return np.sqrt(ss), mx
+
+
+def gemm_noise(aq_rows, as_rows, wq, ws, acc):
+    """Bound on |GPU - exact| of a blocked GEMM output: 6 RMS of the
+    independent block errors, at least twice the worst single-block error,
+    plus FP32 accumulation."""
+    root, mx = block_abs_sums(aq_rows, as_rows, wq, ws)
+    kb = np.asarray(aq_rows).shape[1] // 128
+    return (np.maximum(6 * MFMA_BLOCK_RMS * root, 2 * MFMA_BLOCK_MAX * mx)
+            + kb * 2.0 ** -24 * np.abs(acc))
+
+
+def e4m3_spacing(v):
+    """Distance between neighbouring E4M3 values at magnitude |v|."""
+    v = np.abs(np.asarray(v, np.float64))
+    _, p = np.frexp(np.maximum(v, 1e-300))
+    return np.ldexp(1.0, np.maximum(p - 1, -6) - 3)
+
+
+def h_code_ambiguity(aq_rows, as_rows, w13q, w13s, g, u, h, hs):
+    """(amb, step) for the rows' h codes: amb marks elements whose scaled value
+    lies within the noise band of a rounding midpoint; step bounds how far
+    (in scaled units) a valid code of such an element can be from the oracle's:
+    the GPU code rounds some value inside the band, so the two codes differ by
+    at most twice the band plus one grid spacing (near zero the band can cover
+    several subnormal steps)."""
+    f = w13q.shape[0] // 2
+    g = np.asarray(g, np.float64); u = np.asarray(u, np.float64); h = np.asarray(h, np.float64)
+    e = gemm_noise(aq_rows, as_rows, w13q, w13s, np.concatenate([g, u], axis=1))
+    eg, eu = e[:, :f], e[:, f:]
+    sig = 1.0 / (1.0 + np.exp(-g))
+    dsilu = sig * (1.0 + g * (1.0 - sig))
+    eh = np.abs(u) * np.abs(dsilu) * eg + np.abs(g * sig) * eu + 2.0 ** -22 * np.abs(h)
+    rows = h.shape[0]
+    ht = np.abs(h).reshape(rows, -1, 128)
+    et = eh.reshape(rows, -1, 128)
+    amax = ht.max(-1)
+    # the tile scale is amax/448 of equally noisy values
+    scale_rel = (np.max(ht + et, -1) - amax + np.max(et, -1)) / np.maximum(amax, 1e-300)
+    hsx = np.repeat(np.asarray(hs, np.float64), 128, axis=1)
+    y = np.abs(h) / hsx
+    band = eh / hsx + y * np.repeat(scale_rel, 128, axis=1)
+    sp = e4m3_spacing(y)
+    lo = np.floor(y / sp) * sp
+    sp_below = e4m3_spacing(np.maximum(lo - sp / 4, 0.0))
+    dist = np.minimum(np.abs(y - (lo + sp / 2)), np.abs(y - (lo - sp_below / 2)))
+    step = 2.0 * band + e4m3_spacing(y + band)
+    return dist <= band, step
+
+
+def check_h_codes(gh, hq, amb, step):
+    """Unambiguous codes equal; ambiguous ones within their allowed step."""
+    from oracle import fp8 as ofp8
+    same = gh == hq
+    assert np.all(same | amb), int(np.sum(~same & ~amb))
+    dv = np.abs(ofp8.e4m3_decode(gh) - ofp8.e4m3_decode(hq))
+    assert np.all(dv[~same] <= 1.001 * step[~same])
+    return int(np.sum(~same))
+
+
+def y_allowance(amb, step, hs, w2q, w2s):
+    """Elementwise bound on |delta y| [rows, d] from the ambiguous h codes
+    taking another valid value."""
+    W2 = oquant.dequant_128x128(w2q, w2s)
+    delta = amb * step * np.repeat(np.asarray(hs, np.float64), 128, axis=1)
+    return delta @ np.abs(W2).T
+
+
+def rows_within(got, ref, allow, tol):
+    """Per-row check ||got - ref|| <= tol * ||ref|| + ||allow||; returns
+    (ok mask, relative errors, number of rows that needed the allowance)."""
+    got = np.asarray(got, np.float64); ref = np.asarray(ref, np.float64)
+    err = np.linalg.norm(got - ref, axis=-1)
+    nref = np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
+    nall = np.linalg.norm(allow, axis=-1)
+    ok = err <= tol * nref + nall
+    return ok, err / nref, int(np.sum(err > tol * nref))
+
+
+def layer_allowance(res, experts, T, k, E):
+    """Bound on |delta out| [T, d] of a whole-batch oracle result (moe_layer)
+    from the ambiguous h codes of every expert row, combined with the gates."""
+    rows, d = res["y"].shape
+    allow = np.zeros((rows, d))
+    amb_all = np.zeros(res["hq"].shape, bool)
+    sp_all = np.zeros(res["hq"].shape)
+    off = res["offsets"]
+    for e in range(E + 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        w13q, w13s, w2q, w2s = experts(e)
+        amb, sp = h_code_ambiguity(res["xq_perm"][lo:hi], res["xs_perm"][lo:hi], w13q, w13s,
+                                   res["g"][lo:hi], res["u"][lo:hi], res["h"][lo:hi],
+                                   res["hs"][lo:hi])
+        amb_all[lo:hi], sp_all[lo:hi] = amb, sp
+        allow[lo:hi] = y_allowance(amb, sp, res["hs"][lo:hi], w2q, w2s)
+    w = np.asarray(res["route"]["w"], np.float64)
+    out_allow = np.einsum("tk,tkd->td", np.abs(w), allow[np.asarray(res["pos"], np.int64)])
+    out_allow += allow[T * k:T * k + T]
+    return out_allow, amb_all, sp_all
+
+
+def token_allowance(extra, r, experts, E):
+    """The same bound for tokens evaluated on their own (moe_layer_tokens)."""
+    n, k = r["idx"].shape
+    d = extra["y_shared"].shape[1]
+    out = np.zeros((n, d))
+    for t in range(n):
+        slots = [(r["idx"][t, j], extra["inter_routed"][(t, j)], abs(float(r["w"][t, j])))
+                 for j in range(k)] + [(E, extra["inter_shared"][t], 1.0)]
+        for e, it, wt in slots:
+            w13q, w13s, w2q, w2s = experts(int(e))
+            amb, sp = h_code_ambiguity(extra["xq"][t:t + 1], extra["xs"][t:t + 1], w13q, w13s,
+                                       it["g"], it["u"], it["h"], it["hs"])
+            out[t] += wt * y_allowance(amb, sp, it["hs"], w2q, w2s)[0]
+    return out

@@ -1,0 +1,147 @@
+"""The C ABI loads, exports every declared symbol, and rejects bad arguments
+before touching a GPU (CPU only: nothing here launches a kernel)."""
+
+import ctypes
+import subprocess
+
+import pytest
+
+from routing_fp8_grouped_amd import _lib
+
+P = ctypes.c_void_p
+A = P(0x1000)          # aligned fake device address: never dereferenced by validation
+MIS = P(0x1004)        # misaligned for 16-byte matrices
+MIS4 = P(0x1002)       # misaligned for FP32/int32 arrays
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def last(lib):
+    return lib.moe_last_error().decode()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _lib.header_symbols()
+    assert set(declared) == {"moe_route", "fp8_quant_1x128", "fp8_quant_128x128",
+                             "moe_permute_workspace_bytes", "moe_permute",
+                             "grouped_gemm_fp8_swiglu", "moe_combine", "moe_status_string",
+                             "moe_last_error"}
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
+    assert lib.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+
+
+def rp(E=256, G=8, M=4, k=8, s=2.5):
+    return _lib.RouteParams(E, G, M, k, s)
+
+
+@pytest.mark.parametrize("params,d,code,msg", [
+    (rp(E=0), 256, 1, "n_experts"),
+    (rp(E=300), 256, 1, "n_experts"),
+    (rp(E=250, G=8), 256, 1, "multiple of n_groups"),
+    (rp(M=0), 256, 1, "topk_groups"),
+    (rp(M=9), 256, 1, "topk_groups"),
+    (rp(k=6), 256, 1, "multiple of topk_groups"),
+    (rp(E=16, G=8, M=4, k=12), 256, 1, "exceeds the 2 experts of a group"),
+    (rp(s=float("inf")), 256, 1, "route_scale"),
+    (rp(k=0), 256, 1, "topk"),
+    (rp(E=256, G=1, M=1, k=17), 256, 2, "not implemented"),
+    (rp(), 100, 1, "d=100"),
+    (rp(), 0, 1, "d=0"),
+])
+def test_route_validation(lib, params, d, code, msg):
+    st = lib.moe_route(A, A, None, 10, d, params, A, A, None)
+    assert st == code and msg in last(lib)
+
+
+def test_route_null_and_alignment(lib):
+    assert lib.moe_route(None, A, None, 10, 256, rp(), A, A, None) == 1 and "x is NULL" in last(lib)
+    assert lib.moe_route(A, A, MIS4, 10, 256, rp(), A, A, None) == 1 and "bias" in last(lib)
+    assert lib.moe_route(MIS, A, MIS, 10, 256, rp(), A, A, None) == 1 and "x is not 16" in last(lib)
+    assert lib.moe_route(A, A, None, -1, 256, rp(), A, A, None) == 1
+    # T = 0: successful no-op even with null pointers
+    assert lib.moe_route(None, None, None, 0, 256, rp(), None, None, None) == 0
+
+
+def test_quant_validation(lib):
+    assert lib.fp8_quant_1x128(A, 4, 100, A, A, None) == 1 and "cols=100" in last(lib)
+    assert lib.fp8_quant_1x128(A, -1, 128, A, A, None) == 1
+    assert lib.fp8_quant_1x128(MIS, 4, 128, A, A, None) == 1 and "aligned" in last(lib)
+    assert lib.fp8_quant_1x128(None, 0, 128, None, None, None) == 0
+    assert lib.fp8_quant_128x128(A, 100, 128, A, A, None) == 1 and "N=100" in last(lib)
+    assert lib.fp8_quant_128x128(A, 128, 0, A, A, None) == 1
+    assert lib.fp8_quant_128x128(A, 128 * 70000, 128, A, A, None) == 2
+    assert lib.fp8_quant_128x128(None, 0, 128, None, None, None) == 0
+
+
+def test_permute_validation_and_workspace(lib):
+    need = lib.moe_permute_workspace_bytes(1000, 8, 256)
+    assert need == 4 * 256 * 4          # ceil(1000/256) blocks x E int32
+    assert lib.moe_permute_workspace_bytes(0, 8, 256) == 0
+    args = lambda T=1000, k=8, E=256, ws=A, wsb=need, xq_perm=None: (
+        A, T, k, E, None, None, 0, A, A, A, xq_perm, None, ws, wsb, None)
+    assert lib.moe_permute(*args(E=0)) == 1
+    assert lib.moe_permute(*args(k=17)) == 1
+    assert lib.moe_permute(*args(k=9, E=8)) == 1
+    assert lib.moe_permute(*args(ws=None)) == 3 and "needed" in last(lib)
+    assert lib.moe_permute(*args(wsb=need - 4)) == 3
+    # asking for the row copy requires the quantised inputs and d
+    assert lib.moe_permute(*args(xq_perm=A)) == 1
+    assert lib.moe_permute(*args(T=0, ws=None, wsb=0)) == 0
+
+
+def test_gemm_validation(lib):
+    def call(n_groups=257, rows=100, d=256, f=128, a_rows=10, row_src=A, h=A):
+        return lib.grouped_gemm_fp8_swiglu(A, A, a_rows, row_src, A, n_groups, rows, d, f,
+                                           A, A, A, A, h, A, A, None)
+    assert call(n_groups=0) == 1
+    assert call(n_groups=2000) == 2
+    assert call(d=100) == 1 and "d=100" in last(lib)
+    assert call(f=64) == 1
+    assert call(rows=-1) == 1
+    assert call(a_rows=10, row_src=None) == 1 and "row_src" in last(lib)
+    assert call(h=None) == 1 and "h is NULL" in last(lib)
+    assert call(h=MIS) == 1
+    assert call(rows=0, h=None) == 0
+
+
+def test_combine_validation(lib):
+    assert lib.moe_combine(A, A, A, 10, 0, 256, 80, A, None) == 1
+    assert lib.moe_combine(A, A, A, 10, 8, 100, 80, A, None) == 1
+    assert lib.moe_combine(A, A, A, 10, 8, 256, -2, A, None) == 1
+    assert lib.moe_combine(A, None, A, 10, 8, 256, 80, A, None) == 1 and "pos is NULL" in last(lib)
+    assert lib.moe_combine(None, None, None, 0, 8, 256, 0, None, None) == 0
+
+
+def test_error_is_thread_local(lib):
+    import threading
+    lib.fp8_quant_1x128(A, 4, 100, A, A, None)
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.moe_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "cols=100" in last(lib)
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    import routing_fp8_grouped_amd as moe
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.fp8_quant_1x128(x, torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4, 1))

@@ -154,9 +154,15 @@ def test_sampled_tokens_equal_full_batch():
     cfg, x, wg, b, experts = tiny_problem(T=64)
     res = layer.moe_layer(x, wg, b, experts, cfg.G, cfg.M, cfg.k, 2.5)
     sample = [0, 5, 17, 63]
-    out, r = layer.moe_layer_tokens(x[sample], wg, b, experts, cfg.G, cfg.M, cfg.k, 2.5)
+    out, r, extra = layer.moe_layer_tokens(x[sample], wg, b, experts, cfg.G, cfg.M, cfg.k, 2.5)
     assert np.array_equal(out, res["out"][sample])
     assert np.array_equal(r["idx"], res["route"]["idx"][sample])
+    for i, t in enumerate(sample):
+        for j in range(cfg.k):
+            p = res["pos"][t, j]
+            assert np.array_equal(extra["inter_routed"][(i, j)]["hq"][0], res["hq"][p])
+            assert np.array_equal(extra["y_routed"][i, j], res["y"][p])
+        assert np.array_equal(extra["inter_shared"][i]["h"][0], res["h"][cfg.T * cfg.k + t])
 
 
 def test_flop_figures(golden):
