@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the forward pass of one DeepSeek-V3 MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload uniform_16k]
+
+One step is the whole hot path on one batch of seeded synthetic tokens already
+resident in HBM: moe_route -> fp8_quant_1x128 -> moe_permute ->
+grouped_gemm_fp8_up -> grouped_gemm_fp8_down -> moe_combine.  The expert
+weights are quantised once beforehand (the offline 128x128 step), as for a
+deployed layer.  Prints one JSON line (rank 0).
+
+The default workload is the V3 layer at 16384 tokens with near-uniform expert
+load, the headline case for the grouped FP8 GEMM.  ``roofline`` reports the
+dominant kernel (the first expert GEMM, 2/3 of the FLOPs) against the MI355X
+dense FP8 MFMA peak, timed with HIP events on the stream it runs on;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import routing_fp8_grouped_amd as moe  # noqa: E402
+from routing_fp8_grouped_amd import configs, inputs  # noqa: E402
+
+METRIC = "MoE-layer tokens/s at d=7168,E=256,k=8; FP8 grouped-GEMM % of MFMA peak"
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense E4M3 MFMA
+HBM_PEAK_GBS = 8000.0
+STAGES = ["route", "quant", "permute", "gemm_up", "gemm_down", "combine"]
+GEMM_SOURCES = ["routing_fp8_grouped_amd/csrc/gemm.hip", "routing_fp8_grouped_amd/csrc/common.h"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per launch of the first expert GEMM from the committed PMC
+    summary, if it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"grouped_gemm_up_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def build_weights(cfg):
+    W = moe.MoEWeights.empty(cfg.E + 1, cfg.d, cfg.f)
+    for e in range(cfg.E + 1):
+        w13, w2 = inputs.expert_weights(cfg, e, "cuda")
+        W.quantize_expert(e, w13, w2)
+        del w13, w2
+    torch.cuda.synchronize()
+    return W
+
+
+def cpu_baseline(cfg, n_tokens):
+    """Time the oracle (as it stands) on the first n_tokens tokens of the
+    workload.  The experts those tokens need are quantised by the oracle first
+    (the offline step, untimed); the timed part is routing, activation
+    quantisation, the experts' blocked GEMMs with SwiGLU and requantisation,
+    and the combine."""
+    import concurrent.futures as cf
+    from oracle import layer as olayer, route as oroute
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    x = inputs.activations(cfg, T=n_tokens).float().numpy()
+    wg = inputs.router_weights(cfg).float().numpy()
+    b = inputs.selection_bias(cfg).numpy()
+    r = oroute.route(x, wg, b, cfg.G, cfg.M, cfg.k, cfg.route_scale)
+    need = sorted(set(r["idx"].reshape(-1).tolist()) | {cfg.E})
+    host = {}
+    for e in need:
+        w13, w2 = inputs.expert_weights(cfg, e, "cuda")
+        host[e] = (w13.float().cpu().numpy(), w2.float().cpu().numpy())
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+        q = dict(zip(need, ex.map(lambda e: olayer.quantize_expert(*host[e]), need)))
+    t0 = time.perf_counter()
+    olayer.moe_layer_tokens(x, wg, b, lambda e: q[e], cfg.G, cfg.M, cfg.k, cfg.route_scale)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n_tokens} token(s) of the {cfg.name} workload, whole layer "
+                      f"({len(need)} experts incl. shared), {dt:.1f} s; expert weights "
+                      "quantised by the oracle beforehand (untimed, as on the GPU)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="uniform_16k", choices=sorted(configs.CONFIGS))
+    ap.add_argument("--dispatch", action="store_true",
+                    help="copy the FP8 rows into grouped order instead of gathering in the GEMM")
+    ap.add_argument("--cpu-tokens", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the MoE layer on a single MI355X "
+              "(no sharding or collectives); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = configs.get(args.workload)
+    torch.cuda.set_device(0)
+    log(f"workload {cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E}+1 G={cfg.G} M={cfg.M} k={cfg.k} f={cfg.f}")
+    x, wg, b = (t.cuda() for t in inputs.host_inputs(cfg))
+    W = build_weights(cfg)
+    layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.f, cfg.route_scale,
+                         dispatch=args.dispatch)
+    log("inputs and FP8 weights resident")
+
+    # A plain copy of known size, outside the timed region: its FETCH_SIZE /
+    # WRITE_SIZE counters calibrate the GEMM's.
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)                                        # reads 1 GiB, writes 1 GiB
+    torch.cuda.synchronize()
+    del src, dst
+
+    for _ in range(args.warmup):
+        layer.forward(x, wg, b, W)
+    torch.cuda.synchronize()
+    log(f"{args.warmup} warmup steps done")
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        marks = ev[s]
+        marks[0].record(stream)
+        it = iter(marks[1:])
+        layer.forward(x, wg, b, W, mark=lambda name: next(it).record(stream))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                for i, name in enumerate(STAGES)}
+    log(f"{args.steps} timed steps: {ms_per_step:.3f} ms/step; stages " +
+        ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
+
+    counts = np.bincount(layer.idx.cpu().numpy().reshape(-1), minlength=cfg.E)
+    rows = cfg.rows
+    up_flop = rows * 2 * (2 * cfg.f) * cfg.d
+    down_flop = rows * 2 * cfg.d * cfg.f
+    up_tflops = up_flop / (stage_ms["gemm_up"] * 1e-3) / 1e12
+    gemm_tflops = (up_flop + down_flop) / ((stage_ms["gemm_up"] + stage_ms["gemm_down"]) * 1e-3) / 1e12
+    touched = int((counts > 0).sum()) + 1
+    weight_bytes = touched * (3 * cfg.d * cfg.f + 3 * (cfg.d // 128) * (cfg.f // 128) * 4)
+    traffic = read_traffic(cfg.name)
+    # algorithmic bytes of the first expert GEMM: each touched expert's W1/W3
+    # codes and scales once, the token rows once, h and its scales written once
+    up_bytes = (touched * (2 * cfg.f * cfg.d + (2 * cfg.f // 128) * (cfg.d // 128) * 4)
+                + cfg.T * (cfg.d + cfg.d // 128 * 4) + rows * (cfg.f + cfg.f // 128 * 4))
+    up_s = stage_ms["gemm_up"] * 1e-3
+    if up_flop / up_bytes >= FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        roof = {"bound": "mfma", "achieved": up_flop / up_s / 1e12, "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": up_bytes / up_s / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+
+    result = {
+        "metric": METRIC,
+        "value": cfg.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d,
+                   "routed_experts": cfg.E, "shared_experts": 1, "groups": cfg.G,
+                   "groups_per_token": cfg.M, "topk": cfg.k, "d_ffn": cfg.f,
+                   "route_scale": cfg.route_scale, "dispatch_copy": args.dispatch},
+        "roofline": dict(roof, traffic=traffic,
+                         kernel="grouped_gemm_fp8_up (grouped_gemm_kernel<true>)",
+                         flop_per_launch=up_flop, algorithmic_bytes_per_launch=up_bytes,
+                         avg_launch_ms=stage_ms["gemm_up"], tflops=up_tflops),
+        "stages_ms": stage_ms,
+        "grouped_gemm_tflops": gemm_tflops,
+        "grouped_gemm_frac_of_fp8_peak": gemm_tflops / FP8_PEAK_TFLOPS,
+        "expert_rows": {"max": int(counts.max()), "min": int(counts.min()),
+                        "experts_touched": touched},
+        "weights_hbm_gbs": weight_bytes / (ms_per_step * 1e-3) / 1e9,
+        "context": "pages: 2.788M H800 GPU-hours for the whole V3 training run; "
+                   "180K H800 GPU-hours per trillion training tokens (not comparable)",
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_tokens} token(s)")
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

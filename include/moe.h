@@ -149,6 +149,23 @@ moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, int a_row
                                    const uint8_t* w2, const float* w2_s,
                                    uint8_t* h, float* hs, uint16_t* y, void* stream);
 
+/* grouped_gemm_fp8_up — the first stage of grouped_gemm_fp8_swiglu alone:
+ * G, U, h = SiLU(G) * U and its 1x128 quantisation into (h, hs), same
+ * arguments and rules as above.  Separately callable so that the two expert
+ * GEMMs can be scheduled, timed or recomputed on their own. */
+moe_status grouped_gemm_fp8_up(const uint8_t* aq, const float* as, int a_rows,
+                               const int32_t* row_src, const int32_t* offsets,
+                               int n_groups, int total_rows, int d, int f,
+                               const uint8_t* w13, const float* w13_s,
+                               uint8_t* h, float* hs, void* stream);
+
+/* grouped_gemm_fp8_down — the second stage alone: y = blocked FP8 GEMM of
+ * (h, hs) [total_rows, f] with w2[g] per group, BF16 out [total_rows, d]. */
+moe_status grouped_gemm_fp8_down(const uint8_t* h, const float* hs, const int32_t* offsets,
+                                 int n_groups, int total_rows, int d, int f,
+                                 const uint8_t* w2, const float* w2_s,
+                                 uint16_t* y, void* stream);
+
 /* moe_combine — out[t] = BF16( sum_j w[t][j] * y[pos[t][j]] + y[shared_row0 + t] )
  * (book chapter 7 "Selecting and combining experts"; chapter 15 "What combine
  * must do"), summed in FP32 in slot order.

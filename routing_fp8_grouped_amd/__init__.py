@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import MoEError, RouteParams  # noqa: F401
 
 __all__ = ["moe_route", "fp8_quant_1x128", "fp8_quant_128x128", "moe_permute_workspace_bytes",
-           "moe_permute", "grouped_gemm_fp8_swiglu", "moe_combine", "MoEWeights", "MoELayer",
+           "moe_permute", "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up", "grouped_gemm_fp8_down",
+           "moe_combine", "MoEWeights", "MoELayer",
            "MoEError", "RouteParams"]
 
 
@@ -110,6 +111,33 @@ def grouped_gemm_fp8_swiglu(aq, as_, row_src, offsets, w13, w13_s, w2, w2_s, h, 
         _stream(stream)))
 
 
+def grouped_gemm_fp8_up(aq, as_, row_src, offsets, w13, w13_s, h, hs, stream=None):
+    """First expert GEMM with the SwiGLU epilogue: h/hs [rows, f]."""
+    for t, dt, n in ((aq, torch.uint8, "aq"), (as_, torch.float32, "as"),
+                     (row_src, torch.int32, "row_src"), (offsets, torch.int32, "offsets"),
+                     (w13, torch.uint8, "w13"), (w13_s, torch.float32, "w13_s"),
+                     (h, torch.uint8, "h"), (hs, torch.float32, "hs")):
+        _dev(t, dt, n)
+    n_groups, two_f, d = w13.shape
+    lib = _lib.load()
+    _lib.check("grouped_gemm_fp8_up", lib.grouped_gemm_fp8_up(
+        _ptr(aq), _ptr(as_), aq.shape[0], _ptr(row_src), _ptr(offsets), n_groups, h.shape[0], d,
+        two_f // 2, _ptr(w13), _ptr(w13_s), _ptr(h), _ptr(hs), _stream(stream)))
+
+
+def grouped_gemm_fp8_down(h, hs, offsets, w2, w2_s, y, stream=None):
+    """Second expert GEMM: y [rows, d] BF16."""
+    for t, dt, n in ((h, torch.uint8, "h"), (hs, torch.float32, "hs"),
+                     (offsets, torch.int32, "offsets"), (w2, torch.uint8, "w2"),
+                     (w2_s, torch.float32, "w2_s"), (y, torch.bfloat16, "y")):
+        _dev(t, dt, n)
+    n_groups, d, f = w2.shape
+    lib = _lib.load()
+    _lib.check("grouped_gemm_fp8_down", lib.grouped_gemm_fp8_down(
+        _ptr(h), _ptr(hs), _ptr(offsets), n_groups, h.shape[0], d, f, _ptr(w2), _ptr(w2_s),
+        _ptr(y), _stream(stream)))
+
+
 def moe_combine(y, pos, w, shared_row0, out, stream=None):
     """out [T, d] = BF16(sum_j w[t, j] * y[pos[t, j]] + y[shared_row0 + t])."""
     _dev(y, torch.bfloat16, "y"); _dev(pos, torch.int32, "pos"); _dev(w, torch.float32, "w")
@@ -172,21 +200,30 @@ class MoELayer:
         self.y = torch.empty(rows, d, dtype=torch.bfloat16, **dev)
         self.out = torch.empty(T, d, dtype=torch.bfloat16, **dev)
 
-    def forward(self, x, wg, bias, weights, stream=None):
+    def forward(self, x, wg, bias, weights, stream=None, mark=None):
+        """Run the layer on x [T, d].  ``mark(name)``, if given, is called after
+        each stage is enqueued (the bench records HIP events there)."""
+        mark = mark or (lambda name: None)
         moe_route(x, wg, bias, self.n_groups, self.topk_groups, self.k, self.route_scale,
                   self.idx, self.w, stream)
+        mark("route")
         fp8_quant_1x128(x, self.xq, self.xs, stream)
+        mark("quant")
         if self.dispatch:
             moe_permute(self.idx, self.E, self.offsets, self.pos, self.row_token, self.ws,
                         self.xq, self.xs, self.xq_perm, self.xs_perm, stream)
-            grouped_gemm_fp8_swiglu(self.xq_perm, self.xs_perm, None, self.offsets, weights.w13q,
-                                    weights.w13s, weights.w2q, weights.w2s, self.h, self.hs, self.y,
-                                    stream)
+            aq, as_, src = self.xq_perm, self.xs_perm, None
         else:
             moe_permute(self.idx, self.E, self.offsets, self.pos, self.row_token, self.ws,
                         stream=stream)
-            grouped_gemm_fp8_swiglu(self.xq, self.xs, self.row_token, self.offsets, weights.w13q,
-                                    weights.w13s, weights.w2q, weights.w2s, self.h, self.hs, self.y,
-                                    stream)
+            aq, as_, src = self.xq, self.xs, self.row_token
+        mark("permute")
+        grouped_gemm_fp8_up(aq, as_, src, self.offsets, weights.w13q, weights.w13s, self.h,
+                            self.hs, stream)
+        mark("gemm_up")
+        grouped_gemm_fp8_down(self.h, self.hs, self.offsets, weights.w2q, weights.w2s, self.y,
+                              stream)
+        mark("gemm_down")
         moe_combine(self.y, self.pos, self.w, self.T * self.k, self.out, stream)
+        mark("combine")
         return self.out

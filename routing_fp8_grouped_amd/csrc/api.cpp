@@ -177,18 +177,20 @@ moe_status moe_permute(const int32_t* idx, int T, int k, int E, const uint8_t* x
                     "moe_permute launch");
 }
 
-moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, int a_rows,
-                                   const int32_t* row_src, const int32_t* offsets, int n_groups,
-                                   int total_rows, int d, int f, const uint8_t* w13,
-                                   const float* w13_s, const uint8_t* w2, const float* w2_s,
-                                   uint8_t* h, float* hs, uint16_t* y, void* stream) {
-  clear_error();
+namespace {
+
+moe_status check_gemm_shape(int n_groups, int total_rows, int d, int f) {
   REQUIRE(n_groups >= 1, "n_groups=%d must be >= 1", n_groups);
   if (n_groups > 1024) return fail(MOE_ERR_UNSUPPORTED, "n_groups=%d > 1024", n_groups);
   REQUIRE(total_rows >= 0, "total_rows=%d is negative", total_rows);
   REQUIRE(d >= 128 && d % 128 == 0, "d=%d must be a positive multiple of 128", d);
   REQUIRE(f >= 128 && f % 128 == 0, "f=%d must be a positive multiple of 128", f);
-  if (total_rows == 0) return MOE_OK;
+  return MOE_OK;
+}
+
+moe_status check_up(const uint8_t* aq, const float* as, int a_rows, const int32_t* row_src,
+                    const int32_t* offsets, int total_rows, const uint8_t* w13, const float* w13_s,
+                    uint8_t* h, float* hs) {
   REQUIRE(a_rows >= 1, "a_rows=%d must be >= 1", a_rows);
   REQUIRE(row_src != nullptr || a_rows >= total_rows,
           "a_rows=%d < total_rows=%d without row_src", a_rows, total_rows);
@@ -198,15 +200,71 @@ moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, int a_row
   REQUIRE_PTR4(offsets);
   REQUIRE_PTR(w13);
   REQUIRE_PTR4(w13_s);
-  REQUIRE_PTR(w2);
-  REQUIRE_PTR4(w2_s);
   REQUIRE_PTR(h);
   REQUIRE_PTR4(hs);
+  return MOE_OK;
+}
+
+moe_status check_down(const uint8_t* h, const float* hs, const int32_t* offsets, const uint8_t* w2,
+                      const float* w2_s, uint16_t* y) {
+  REQUIRE_PTR(h);
+  REQUIRE_PTR4(hs);
+  REQUIRE_PTR4(offsets);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR4(w2_s);
   REQUIRE_PTR(y);
-  return hip_status(moe::launch_grouped_gemm(aq, as, row_src, offsets, n_groups, total_rows, d, f,
-                                             w13, w13_s, w2, w2_s, h, hs, y,
-                                             static_cast<hipStream_t>(stream), a_rows),
-                    "grouped_gemm_fp8_swiglu launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status grouped_gemm_fp8_up(const uint8_t* aq, const float* as, int a_rows,
+                               const int32_t* row_src, const int32_t* offsets, int n_groups,
+                               int total_rows, int d, int f, const uint8_t* w13,
+                               const float* w13_s, uint8_t* h, float* hs, void* stream) {
+  clear_error();
+  moe_status s = check_gemm_shape(n_groups, total_rows, d, f);
+  if (s != MOE_OK || total_rows == 0) return s;
+  s = check_up(aq, as, a_rows, row_src, offsets, total_rows, w13, w13_s, h, hs);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_gemm_up(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d,
+                                        f, w13, w13_s, h, hs, static_cast<hipStream_t>(stream)),
+                    "grouped_gemm_fp8_up launch");
+}
+
+moe_status grouped_gemm_fp8_down(const uint8_t* h, const float* hs, const int32_t* offsets,
+                                 int n_groups, int total_rows, int d, int f, const uint8_t* w2,
+                                 const float* w2_s, uint16_t* y, void* stream) {
+  clear_error();
+  moe_status s = check_gemm_shape(n_groups, total_rows, d, f);
+  if (s != MOE_OK || total_rows == 0) return s;
+  s = check_down(h, hs, offsets, w2, w2_s, y);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_gemm_down(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y,
+                                          static_cast<hipStream_t>(stream)),
+                    "grouped_gemm_fp8_down launch");
+}
+
+moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, int a_rows,
+                                   const int32_t* row_src, const int32_t* offsets, int n_groups,
+                                   int total_rows, int d, int f, const uint8_t* w13,
+                                   const float* w13_s, const uint8_t* w2, const float* w2_s,
+                                   uint8_t* h, float* hs, uint16_t* y, void* stream) {
+  clear_error();
+  moe_status s = check_gemm_shape(n_groups, total_rows, d, f);
+  if (s != MOE_OK || total_rows == 0) return s;
+  s = check_up(aq, as, a_rows, row_src, offsets, total_rows, w13, w13_s, h, hs);
+  if (s != MOE_OK) return s;
+  s = check_down(h, hs, offsets, w2, w2_s, y);
+  if (s != MOE_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  s = hip_status(moe::launch_gemm_up(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d, f,
+                                     w13, w13_s, h, hs, st),
+                 "grouped_gemm_fp8_swiglu launch (up)");
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_gemm_down(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y,
+                                          st),
+                    "grouped_gemm_fp8_swiglu launch (down)");
 }
 
 moe_status moe_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k, int d,

@@ -82,12 +82,109 @@ __device__ __forceinline__ int frag_row(int wn, int ns) {
   return wn * 128 + ns * 16;
 }
 
-struct Prefetch {
+// Source pointers of one thread's load slots for the current tile.
+struct TileSrc {
+  const uint8_t* a[4];   // activation rows: 4 16-byte chunks per K block
+  const uint8_t* b[8];   // weight rows: 8 16-byte chunks per K block
+  const float* sa;       // activation scales of row tid (tid < 128)
+  const float* sw0;      // weight scales of this wave's two 128-row blocks
+  const float* sw1;
+  uint32_t b_ok;         // bit it: weight row of slot it exists
+};
+
+// Registers holding one K block in flight between global memory and LDS.
+struct Stage {
   uint4 a[4];
   uint4 b[8];
-  float sa;
-  float sw0, sw1;
+  float sa, sw0, sw1;
 };
+
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int* smTile, int NT, long l) {
+  const int q = (int)(l / NT);
+  int a = 0, b = p.n_groups - 1;
+  while (a < b) {
+    const int mid = (a + b + 1) >> 1;
+    if (smTile[mid] <= q) a = mid; else b = mid - 1;
+  }
+  Tile t;
+  t.g = a;
+  const int mtg = smTile[a + 1] - smTile[a];
+  const int local = (int)(l - (long)smTile[a] * NT);
+  t.n = local / mtg;
+  const int m = local - t.n * mtg;
+  t.row0 = p.offsets[a] + m * GM;
+  // rows past total_rows (only possible with malformed offsets) are never touched
+  t.rows_valid = min(GM, min(p.offsets[a + 1], p.total_rows) - t.row0);
+  return t;
+}
+
+template <bool SWIGLU>
+__device__ __forceinline__ TileSrc tile_sources(const GemmArgs& p, const Tile& t, int tid, int wn) {
+  TileSrc s;
+  const int KS = p.K / GK;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
+    int row = min(max(t.row0 + min(r, t.rows_valid - 1), 0), p.total_rows - 1);
+    if (p.row_src) row = p.row_src[row];
+    row = min(max(row, 0), p.a_rows - 1);
+    s.a[it] = p.a + (size_t)row * p.K + c * 16;
+  }
+  {
+    int srow = min(max(t.row0 + min(tid & (GM - 1), t.rows_valid - 1), 0), p.total_rows - 1);
+    if (p.row_src) srow = p.row_src[srow];
+    srow = min(max(srow, 0), p.a_rows - 1);
+    s.sa = p.as + (size_t)srow * KS;
+  }
+  s.b_ok = 0;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int rr = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
+    const int wr = weight_row<SWIGLU>(p, t.n, rr);
+    const bool ok = wr < p.N;
+    s.b_ok |= (ok ? 1u : 0u) << it;
+    s.b[it] = p.b + ((size_t)t.g * p.N + (ok ? wr : 0)) * p.K + c * 16;
+  }
+  const int nsb = p.N / 128;
+  int sb0, sb1;
+  if (SWIGLU) {
+    sb0 = t.n;
+    sb1 = p.f / 128 + t.n;
+  } else {
+    sb0 = sb1 = min(2 * t.n + wn, nsb - 1);
+  }
+  s.sw0 = p.bs + ((size_t)t.g * nsb + sb0) * KS;
+  s.sw1 = p.bs + ((size_t)t.g * nsb + sb1) * KS;
+  return s;
+}
+
+__device__ __forceinline__ void issue_loads(const TileSrc& s, int kb, int tid, Stage& st) {
+  const size_t off = (size_t)kb * GK;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) st.a[it] = *reinterpret_cast<const uint4*>(s.a[it] + off);
+#pragma unroll
+  for (int it = 0; it < 8; ++it)
+    st.b[it] = ((s.b_ok >> it) & 1u) ? *reinterpret_cast<const uint4*>(s.b[it] + off)
+                                     : make_uint4(0, 0, 0, 0);
+  st.sa = s.sa[kb];
+  st.sw0 = s.sw0[kb];
+  st.sw1 = s.sw1[kb];
+}
+
+__device__ __forceinline__ void commit_stage(const Stage& st, int tid, unsigned char* A,
+                                             unsigned char* B, float* SA) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
+    *reinterpret_cast<uint4*>(A + op_off(r, c)) = st.a[it];
+  }
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int rr = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
+    *reinterpret_cast<uint4*>(B + op_off(rr, c)) = st.b[it];
+  }
+  if (tid < GM) SA[tid] = st.sa;
+}
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
@@ -132,104 +229,18 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) 
   long L = lo + slot;
   if (L >= hi) return;
 
-  auto decode = [&](long l) {
-    const int q = (int)(l / NT);
-    int a = 0, b = p.n_groups - 1;
-    while (a < b) {
-      const int mid = (a + b + 1) >> 1;
-      if (smTile[mid] <= q) a = mid; else b = mid - 1;
-    }
-    Tile t;
-    t.g = a;
-    const int mtg = smTile[a + 1] - smTile[a];
-    const int local = (int)(l - (long)smTile[a] * NT);
-    t.n = local / mtg;
-    const int m = local - t.n * mtg;
-    t.row0 = p.offsets[a] + m * GM;
-    // rows past total_rows (only possible with malformed offsets) are never touched
-    t.rows_valid = min(GM, min(p.offsets[a + 1], p.total_rows) - t.row0);
-    return t;
-  };
-
-  // Per-tile source pointers of this thread's load slots.
-  const uint8_t* a_ptr[4];
-  const uint8_t* b_ptr[8];
-  bool b_ok[8];
-  const float* sa_ptr = nullptr;
-  const float* sw_ptr0 = nullptr;
-  const float* sw_ptr1 = nullptr;
-  const int KS = KB;  // scales per row
-  auto setup = [&](const Tile& t) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int r = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
-      int row = min(max(t.row0 + min(r, t.rows_valid - 1), 0), p.total_rows - 1);
-      if (p.row_src) row = p.row_src[row];
-      row = min(max(row, 0), p.a_rows - 1);
-      a_ptr[it] = p.a + (size_t)row * p.K + c * 16;
-      if (it == 0 && tid < GM) {
-        int srow = min(max(t.row0 + min(tid, t.rows_valid - 1), 0), p.total_rows - 1);
-        if (p.row_src) srow = p.row_src[srow];
-        srow = min(max(srow, 0), p.a_rows - 1);
-        sa_ptr = p.as + (size_t)srow * KS;
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int rr = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
-      const int wr = weight_row<SWIGLU>(p, t.n, rr);
-      b_ok[it] = wr < p.N;
-      b_ptr[it] = p.b + ((size_t)t.g * p.N + (b_ok[it] ? wr : 0)) * p.K + c * 16;
-    }
-    const int nsb = p.N / 128;
-    int sb0, sb1;
-    if (SWIGLU) {
-      sb0 = t.n;
-      sb1 = p.f / 128 + t.n;
-    } else {
-      sb0 = sb1 = min(2 * t.n + wn, nsb - 1);
-    }
-    sw_ptr0 = p.bs + ((size_t)t.g * nsb + sb0) * KS;
-    sw_ptr1 = p.bs + ((size_t)t.g * nsb + sb1) * KS;
-  };
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  auto issue = [&](Prefetch& f, int kb) {
-    const size_t off = (size_t)kb * GK;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) f.a[it] = *reinterpret_cast<const uint4*>(a_ptr[it] + off);
-#pragma unroll
-    for (int it = 0; it < 8; ++it)
-      f.b[it] = b_ok[it] ? *reinterpret_cast<const uint4*>(b_ptr[it] + off) : zero4;
-    f.sa = (tid < GM) ? sa_ptr[kb] : 0.0f;
-    f.sw0 = sw_ptr0[kb];
-    f.sw1 = sw_ptr1[kb];
-  };
-  auto commit = [&](const Prefetch& f, int buf) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int r = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
-      *reinterpret_cast<uint4*>(&smA[buf][op_off(r, c)]) = f.a[it];
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int rr = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
-      *reinterpret_cast<uint4*>(&smB[buf][op_off(rr, c)]) = f.b[it];
-    }
-    if (tid < GM) smSA[buf][tid] = f.sa;
-  };
-
   v4f acc[4][8];
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
     for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  Tile cur = decode(L);
-  setup(cur);
-  Prefetch pf;
-  issue(pf, 0);
-  float sw0 = pf.sw0, sw1 = pf.sw1;
-  commit(pf, 0);
+  Tile cur = decode_tile(p, smTile, NT, L);
+  TileSrc src = tile_sources<SWIGLU>(p, cur, tid, wn);
+  Stage st;
+  issue_loads(src, 0, tid, st);
+  float sw0 = st.sw0, sw1 = st.sw1;
+  commit_stage(st, tid, smA[0], smB[0], smSA[0]);
   __syncthreads();
   int buf = 0, kb = 0;
 
@@ -244,11 +255,11 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) 
       nL = L + nslot;
       has_next = nL < hi;
       if (has_next) {
-        nxt = decode(nL);
-        setup(nxt);
+        nxt = decode_tile(p, smTile, NT, nL);
+        src = tile_sources<SWIGLU>(p, nxt, tid, wn);
       }
     }
-    if (has_next) issue(pf, nkb);
+    if (has_next) issue_loads(src, nkb, tid, st);
 
     // ---- multiply the current K block ----
     {
@@ -379,9 +390,9 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) 
     }
 
     if (!has_next) break;
-    commit(pf, buf ^ 1);
-    sw0 = pf.sw0;
-    sw1 = pf.sw1;
+    commit_stage(st, tid, smA[buf ^ 1], smB[buf ^ 1], smSA[buf ^ 1]);
+    sw0 = st.sw0;
+    sw1 = st.sw1;
     __syncthreads();
     buf ^= 1;
     kb = nkb;
@@ -404,11 +415,10 @@ static int num_cus() {
   return g_num_cus[dev];
 }
 
-hipError_t launch_grouped_gemm(const uint8_t* aq, const float* as, const int32_t* row_src,
-                               const int32_t* offsets, int n_groups, int total_rows, int d, int f,
-                               const uint8_t* w13, const float* w13_s, const uint8_t* w2,
-                               const float* w2_s, uint8_t* h, float* hs, uint16_t* y,
-                               hipStream_t stream, int a_rows) {
+hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const int32_t* row_src,
+                          const int32_t* offsets, int n_groups, int total_rows, int d, int f,
+                          const uint8_t* w13, const float* w13_s, uint8_t* h, float* hs,
+                          hipStream_t stream) {
   const int grid = ((num_cus() + 7) / 8) * 8;
   GemmArgs s1{};
   s1.a = aq;
@@ -427,8 +437,13 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const float* as, const int32_t
   s1.h = h;
   s1.hs = hs;
   hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(grid), dim3(G_THREADS), 0, stream, s1);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* offsets, int n_groups,
+                            int total_rows, int d, int f, const uint8_t* w2, const float* w2_s,
+                            uint16_t* y, hipStream_t stream) {
+  const int grid = ((num_cus() + 7) / 8) * 8;
   GemmArgs s2{};
   s2.a = h;
   s2.as = hs;

@@ -24,11 +24,13 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const uint8_t
                           int32_t* row_token, uint8_t* xq_perm, float* xs_perm, void* ws,
                           hipStream_t stream);
 
-hipError_t launch_grouped_gemm(const uint8_t* aq, const float* as, const int32_t* row_src,
-                               const int32_t* offsets, int n_groups, int total_rows, int d, int f,
-                               const uint8_t* w13, const float* w13_s, const uint8_t* w2,
-                               const float* w2_s, uint8_t* h, float* hs, uint16_t* y,
-                               hipStream_t stream, int a_rows);
+hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const int32_t* row_src,
+                          const int32_t* offsets, int n_groups, int total_rows, int d, int f,
+                          const uint8_t* w13, const float* w13_s, uint8_t* h, float* hs,
+                          hipStream_t stream);
+hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* offsets, int n_groups,
+                            int total_rows, int d, int f, const uint8_t* w2, const float* w2_s,
+                            uint16_t* y, hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k,
                           int d, int shared_row0, uint16_t* out, hipStream_t stream);

@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol(lib):
     declared = _lib.header_symbols()
     assert set(declared) == {"moe_route", "fp8_quant_1x128", "fp8_quant_128x128",
                              "moe_permute_workspace_bytes", "moe_permute",
-                             "grouped_gemm_fp8_swiglu", "moe_combine", "moe_status_string",
+                             "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up",
+                             "grouped_gemm_fp8_down", "moe_combine", "moe_status_string",
                              "moe_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -115,6 +116,15 @@ def test_gemm_validation(lib):
     assert call(h=None) == 1 and "h is NULL" in last(lib)
     assert call(h=MIS) == 1
     assert call(rows=0, h=None) == 0
+    # the two stages validate the same way
+    up = lambda rows=100, d=256, h=A, row_src=A: lib.grouped_gemm_fp8_up(
+        A, A, 10, row_src, A, 257, rows, d, 128, A, A, h, A, None)
+    assert up(d=100) == 1 and up(h=None) == 1 and up(row_src=None) == 1
+    assert up(rows=0, h=None) == 0
+    down = lambda rows=100, f=128, y=A: lib.grouped_gemm_fp8_down(
+        A, A, A, 257, rows, 256, f, A, A, y, None)
+    assert down(f=100) == 1 and down(y=MIS) == 1 and "y is not 16" in last(lib)
+    assert down(rows=0, y=None) == 0
 
 
 def test_combine_validation(lib):
