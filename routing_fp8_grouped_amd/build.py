@@ -36,6 +36,9 @@ def _compile(src, extra):
     cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
            "-I", INCLUDE, "-I", CSRC,
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA results in VGPRs: the FP32 promotion reads them without
+           # v_accvgpr_read copies
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wno-unused-command-line-argument",
            "-c", os.path.join(CSRC, src), "-o", obj] + extra
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -56,7 +56,14 @@ struct GemmArgs {
   uint16_t* y;              // stage 2 out [rows, N]
 };
 
-__device__ __forceinline__ int op_off(int r, int c) { return r * GK + ((c ^ ((r >> 1) & 7)) << 4); }
+// LDS layout of a 128-byte operand row r: its 16-byte chunk c sits at chunk
+// position c ^ swz(r).  A fragment read (ds_read_b128) has lanes 0..15 on rows
+// r0..r0+15 at one chunk; swz gives rows r0..r0+7 eight different positions
+// (conflict-free when 8 lanes are served per cycle) and gives the even rows
+// and the odd rows of r0..r0+15 eight positions each (conflict-free when 16
+// lanes are served per cycle over 64 banks).
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+__device__ __forceinline__ int op_off(int r, int c) { return r * GK + ((c ^ swz(r)) << 4); }
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -82,118 +89,183 @@ __device__ __forceinline__ int frag_row(int wn, int ns) {
   return wn * 128 + ns * 16;
 }
 
-// Source pointers of one thread's load slots for the current tile.
-struct TileSrc {
-  const uint8_t* a[4];   // activation rows: 4 16-byte chunks per K block
-  const uint8_t* b[8];   // weight rows: 8 16-byte chunks per K block
-  const float* sa;       // activation scales of row tid (tid < 128)
-  const float* sw0;      // weight scales of this wave's two 128-row blocks
-  const float* sw1;
-  uint32_t b_ok;         // bit it: weight row of slot it exists
-};
+// ---- LDS ring: NSTAGE K blocks in flight, filled by direct global->LDS loads ----
+constexpr int NSTAGE = 3;
+constexpr int ST_A = GM * GK;                   // activation tile, 16 KB
+constexpr int ST_B = GNB * GK;                  // weight tile, 32 KB
+constexpr int ST_SA = 256 * 4;                  // activation scales (rows 0..127; 128..255 spare)
+constexpr int ST_SW = 4 * 256;                  // per wave: its two weight-block scales
+constexpr int ST_BYTES = ST_A + ST_B + ST_SA + ST_SW;
+// DMA instructions per wave per K block: 4 (A) + 8 (B) + 1 (SA) + 1 (SW).
+constexpr int DMA_PER_STAGE = 14;
 
-// Registers holding one K block in flight between global memory and LDS.
-struct Stage {
-  uint4 a[4];
-  uint4 b[8];
-  float sa, sw0, sw1;
-};
+// Direct global->LDS loads.  Lane l of the wave writes its 16 (or 4) bytes at
+// LDS byte address lds + 16 l (4 l); the source address is per lane.  They are
+// issued from inline assembly so that the compiler does not track them: it
+// would otherwise make every later LDS read wait for all of them, which would
+// drain the pipeline each K block.  The instructions have no register outputs
+// (the data goes to LDS); every LDS read of their data follows an explicit
+// vmcnt wait and a barrier below, and every reuse of a ring slot follows a
+// barrier.  M0 carries the LDS address; the compiler does not allocate it.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+// base: wave-uniform global address; off: per-lane byte offset (32 bits).
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
 
-__device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int* smTile, int NT, long l) {
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | (((N >> 4) & 3) << 14));
+}
+
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* __restrict__ offsets,
+                                            const int* smTile, int NT, long l) {
   const int q = (int)(l / NT);
   int a = 0, b = p.n_groups - 1;
   while (a < b) {
     const int mid = (a + b + 1) >> 1;
     if (smTile[mid] <= q) a = mid; else b = mid - 1;
   }
+  a = __builtin_amdgcn_readfirstlane(a);   // uniform: offsets come through scalar loads
   Tile t;
   t.g = a;
-  const int mtg = smTile[a + 1] - smTile[a];
+  const int mtg = __builtin_amdgcn_readfirstlane(smTile[a + 1] - smTile[a]);
   const int local = (int)(l - (long)smTile[a] * NT);
   t.n = local / mtg;
   const int m = local - t.n * mtg;
-  t.row0 = p.offsets[a] + m * GM;
+  t.row0 = offsets[a] + m * GM;
   // rows past total_rows (only possible with malformed offsets) are never touched
-  t.rows_valid = min(GM, min(p.offsets[a + 1], p.total_rows) - t.row0);
+  t.rows_valid = min(GM, min(offsets[a + 1], p.total_rows) - t.row0);
   return t;
 }
 
+// Per-lane global sources of one wave's DMA instructions for a tile; the K block
+// offset is added at issue time.  LDS destinations are fixed: instruction i of
+// wave w writes 1 KB at (w * n_i + i) KB of its region, lane l 16 bytes at
+// 16 l, i.e. row 8 (w * n_i + i) + l / 8, physical chunk l % 8, which holds the
+// logical chunk (l % 8) ^ swz(row) (the swizzle is applied on the
+// source side).
+struct TileSrc {
+  uint32_t a[4];          // byte offsets into p.a
+  uint32_t b[8];          // byte offsets into the group's weights
+  uint32_t sa;            // byte offset into p.as
+  uint32_t sw;            // byte offset into p.bs
+  const uint8_t* bbase;   // the group's weights (uniform)
+};
+
+// Source rows (in p.a) of this lane's 4 activation DMA rows and its scale row.
+struct TileRows {
+  int a[4];
+  int sa;
+};
+
+// Row of p.a holding tile row r (rows past the group's end repeat its last row).
+__device__ __forceinline__ int tile_row(const GemmArgs& p, const Tile& t, int r) {
+  return min(max(t.row0 + min(r, t.rows_valid - 1), 0), p.total_rows - 1);
+}
+
+// Gather indices of a tile's 128 rows, DMA'd into an LDS table one tile ahead
+// (lane l of wave w fetches row_src of tile row (w & 1) * 64 + l; waves 2 and 3
+// repeat waves 0 and 1), so no register ever waits on them.
+__device__ __forceinline__ void dma_tile_rows(const GemmArgs& p, const Tile& t, int wave, int lane,
+                                              unsigned char* table) {
+  const int r = (wave & 1) * 64 + lane;
+  dma4(p.row_src, (uint32_t)tile_row(p, t, r) * 4u, lds_addr(table + (wave & 1) * 256));
+}
+
+__device__ __forceinline__ TileRows tile_rows(const GemmArgs& p, const Tile& t, const int* table,
+                                              int wave, int lane) {
+  TileRows r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = (wave * 4 + i) * 8 + (lane >> 3);
+    r.a[i] = p.row_src ? table[rr] : tile_row(p, t, rr);
+  }
+  const int rs = (wave & 1) * 64 + lane;
+  r.sa = p.row_src ? table[rs] : tile_row(p, t, rs);
+  return r;
+}
+
 template <bool SWIGLU>
-__device__ __forceinline__ TileSrc tile_sources(const GemmArgs& p, const Tile& t, int tid, int wn) {
+__device__ __forceinline__ TileSrc tile_sources(const GemmArgs& p, const Tile& t, const TileRows& rows,
+                                                int wave, int lane) {
   TileSrc s;
   const int KS = p.K / GK;
+  const int pc = lane & 7;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int r = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
-    int row = min(max(t.row0 + min(r, t.rows_valid - 1), 0), p.total_rows - 1);
-    if (p.row_src) row = p.row_src[row];
-    row = min(max(row, 0), p.a_rows - 1);
-    s.a[it] = p.a + (size_t)row * p.K + c * 16;
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 8 + (lane >> 3);
+    const int c = pc ^ swz(r);
+    const int row = min(max(rows.a[i], 0), p.a_rows - 1);
+    s.a[i] = (uint32_t)row * (uint32_t)p.K + c * 16;
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = (wave * 8 + i) * 8 + (lane >> 3);
+    const int c = pc ^ swz(rr);
+    int wr = weight_row<SWIGLU>(p, t.n, rr);
+    if (wr >= p.N) wr = 0;   // padding rows of a partial tile: any valid row, never stored
+    s.b[i] = (uint32_t)wr * (uint32_t)p.K + c * 16;
+  }
+  s.bbase = p.b + (size_t)t.g * p.N * p.K;
+  s.sa = (uint32_t)min(max(rows.sa, 0), p.a_rows - 1) * (uint32_t)(KS * 4);
   {
-    int srow = min(max(t.row0 + min(tid & (GM - 1), t.rows_valid - 1), 0), p.total_rows - 1);
-    if (p.row_src) srow = p.row_src[srow];
-    srow = min(max(srow, 0), p.a_rows - 1);
-    s.sa = p.as + (size_t)srow * KS;
+    // even lanes: this wave's first weight-scale block, odd lanes: its second
+    const int nsb = p.N / 128;
+    const int wn = wave & 1;
+    int sb;
+    if (SWIGLU) sb = (lane & 1) ? p.f / 128 + t.n : t.n;
+    else sb = min(2 * t.n + wn, nsb - 1);
+    s.sw = (uint32_t)(t.g * nsb + sb) * (uint32_t)(KS * 4);
   }
-  s.b_ok = 0;
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int rr = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
-    const int wr = weight_row<SWIGLU>(p, t.n, rr);
-    const bool ok = wr < p.N;
-    s.b_ok |= (ok ? 1u : 0u) << it;
-    s.b[it] = p.b + ((size_t)t.g * p.N + (ok ? wr : 0)) * p.K + c * 16;
-  }
-  const int nsb = p.N / 128;
-  int sb0, sb1;
-  if (SWIGLU) {
-    sb0 = t.n;
-    sb1 = p.f / 128 + t.n;
-  } else {
-    sb0 = sb1 = min(2 * t.n + wn, nsb - 1);
-  }
-  s.sw0 = p.bs + ((size_t)t.g * nsb + sb0) * KS;
-  s.sw1 = p.bs + ((size_t)t.g * nsb + sb1) * KS;
   return s;
 }
 
-__device__ __forceinline__ void issue_loads(const TileSrc& s, int kb, int tid, Stage& st) {
-  const size_t off = (size_t)kb * GK;
+__device__ __forceinline__ void issue_stage(const GemmArgs& p, const TileSrc& s, int kb, int wave,
+                                            unsigned char* stage) {
+  const uint32_t base = lds_addr(stage);
+  const uint8_t* a = p.a + (size_t)kb * GK;
+  const uint8_t* b = s.bbase + (size_t)kb * GK;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) st.a[it] = *reinterpret_cast<const uint4*>(s.a[it] + off);
+  for (int i = 0; i < 4; ++i) dma16(a, s.a[i], base + (wave * 4 + i) * 1024);
 #pragma unroll
-  for (int it = 0; it < 8; ++it)
-    st.b[it] = ((s.b_ok >> it) & 1u) ? *reinterpret_cast<const uint4*>(s.b[it] + off)
-                                     : make_uint4(0, 0, 0, 0);
-  st.sa = s.sa[kb];
-  st.sw0 = s.sw0[kb];
-  st.sw1 = s.sw1[kb];
+  for (int i = 0; i < 8; ++i) dma16(b, s.b[i], base + ST_A + (wave * 8 + i) * 1024);
+  dma4(p.as + kb, s.sa, base + ST_A + ST_B + (wave & 1) * 256);
+  dma4(p.bs + kb, s.sw, base + ST_A + ST_B + ST_SA + wave * 256);
 }
 
-__device__ __forceinline__ void commit_stage(const Stage& st, int tid, unsigned char* A,
-                                             unsigned char* B, float* SA) {
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int r = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
-    *reinterpret_cast<uint4*>(A + op_off(r, c)) = st.a[it];
-  }
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int rr = (tid + G_THREADS * it) >> 3, c = (tid + G_THREADS * it) & 7;
-    *reinterpret_cast<uint4*>(B + op_off(rr, c)) = st.b[it];
-  }
-  if (tid < GM) SA[tid] = st.sa;
+// Barrier for LDS data only: waits for this wave's LDS operations, not for the
+// DMA loads in flight (a __syncthreads() fence would drain those too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
 }
 
 template <bool SWIGLU>
-__global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smA[2][GM * GK];
-  __shared__ __attribute__((aligned(16))) unsigned char smB[2][GNB * GK];
-  __shared__ float smSA[2][GM];
-  __shared__ __attribute__((aligned(16))) unsigned char smE[4][4096];
+__global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p,
+                                                                    const int32_t* __restrict__ offsets) {
+  __shared__ __attribute__((aligned(16))) unsigned char sm[NSTAGE * ST_BYTES];
   __shared__ float smAmax[2][GM];
   __shared__ int smTile[G_MAX_GROUPS + 1];
+  __shared__ __attribute__((aligned(16))) int smRows[2][GM];   // gather indices, by tile parity
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -208,7 +280,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) 
     for (int base = 0; base < p.n_groups; base += 64) {
       const int g = base + lane;
       int mt = 0;
-      if (g < p.n_groups) mt = (p.offsets[g + 1] - p.offsets[g] + GM - 1) / GM;
+      if (g < p.n_groups) mt = (offsets[g + 1] - offsets[g] + GM - 1) / GM;
       int v = mt;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -226,8 +298,50 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) 
   const int slot = blockIdx.x >> 3;
   const int nslot = gridDim.x >> 3;
   const long lo = total * xcd / 8, hi = total * (xcd + 1) / 8;
-  long L = lo + slot;
-  if (L >= hi) return;
+  if (lo + slot >= hi) return;
+
+  // Loader state runs up to two K blocks ahead of the multiply.  When it starts
+  // a tile it builds the tile's DMA sources from the gather table and DMAs the
+  // gather indices of its next tile into the other table; those land before the
+  // next tile starts (every wait below covers all DMAs older than the block
+  // about to be multiplied, and the barrier publishes them to all waves).
+  long ld_L = lo + slot;
+  int ld_kb = 0;
+  int ld_par = 0;
+  bool ld_more = true;   // is there a (tile, K block) at the loader position?
+  Tile ld_tile = decode_tile(p, offsets, smTile, NT, ld_L);
+  TileSrc src;
+  if (p.row_src) {
+    dma_tile_rows(p, ld_tile, wave, lane, reinterpret_cast<unsigned char*>(smRows[0]));
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  }
+#define LOADER_ISSUE(dst)                                                              \
+  do {                                                                                 \
+    if (ld_kb == 0) {                                                                  \
+      src = tile_sources<SWIGLU>(p, ld_tile, tile_rows(p, ld_tile, smRows[ld_par], wave, lane), \
+                                 wave, lane);                                          \
+      if (p.row_src && ld_L + nslot < hi)                                              \
+        dma_tile_rows(p, decode_tile(p, offsets, smTile, NT, ld_L + nslot), wave, lane,         \
+                      reinterpret_cast<unsigned char*>(smRows[ld_par ^ 1]));           \
+    }                                                                                  \
+    issue_stage(p, src, ld_kb, wave, (dst));                                              \
+    if (++ld_kb == KB) {                                                               \
+      ld_kb = 0;                                                                       \
+      ld_L += nslot;                                                                   \
+      ld_par ^= 1;                                                                     \
+      ld_more = ld_L < hi;                                                             \
+      if (ld_more) ld_tile = decode_tile(p, offsets, smTile, NT, ld_L);                         \
+    }                                                                                  \
+  } while (0)
+
+  // prologue: blocks 0 and 1 in flight
+  LOADER_ISSUE(sm);
+  bool next_issued = false;
+  if (ld_more) {
+    LOADER_ISSUE(sm + ST_BYTES);
+    next_issued = true;
+  }
 
   v4f acc[4][8];
 #pragma unroll
@@ -235,46 +349,35 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) 
 #pragma unroll
     for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  Tile cur = decode_tile(p, smTile, NT, L);
-  TileSrc src = tile_sources<SWIGLU>(p, cur, tid, wn);
-  Stage st;
-  issue_loads(src, 0, tid, st);
-  float sw0 = st.sw0, sw1 = st.sw1;
-  commit_stage(st, tid, smA[0], smB[0], smSA[0]);
-  __syncthreads();
-  int buf = 0, kb = 0;
+  long L = lo + slot;
+  Tile cur = decode_tile(p, offsets, smTile, NT, L);
+  int kb = 0;
+  int st = 0;   // ring slot of the block being multiplied
 
   while (true) {
-    // ---- issue the loads of the next (tile, K block) ----
-    int nkb = kb + 1;
-    long nL = L;
-    bool has_next = true;
-    Tile nxt = cur;
-    if (nkb == KB) {
-      nkb = 0;
-      nL = L + nslot;
-      has_next = nL < hi;
-      if (has_next) {
-        nxt = decode_tile(p, smTile, NT, nL);
-        src = tile_sources<SWIGLU>(p, nxt, tid, wn);
-      }
+    // block `st` has landed once at most the next block's DMAs are outstanding
+    if (next_issued) wait_vmcnt<DMA_PER_STAGE>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();   // all lanes' DMAs visible; slot st+2 free again
+    bool issued2 = false;
+    if (ld_more) {
+      LOADER_ISSUE(sm + ((st + 2) % NSTAGE) * ST_BYTES);
+      issued2 = true;
     }
-    if (has_next) issue_loads(src, nkb, tid, st);
 
-    // ---- multiply the current K block ----
+    // ---- multiply block `st` ----
     {
-      const unsigned char* A = smA[buf];
-      const unsigned char* B = smB[buf];
-      float c0[4][4], c1[4][4];
+      const unsigned char* A = sm + st * ST_BYTES;
+      const unsigned char* B = A + ST_A;
+      const float* SA = reinterpret_cast<const float*>(B + ST_B);
+      const float* SW = reinterpret_cast<const float*>(B + ST_B + ST_SA + wave * 256);
+      const float sw0 = SW[0], sw1 = SW[1];
+      float sv[4][4], c[4][4];
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms) {
-        const float4 s4 = *reinterpret_cast<const float4*>(&smSA[buf][wm * 64 + ms * 16 + g16 * 4]);
-        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+        const float4 s4 = *reinterpret_cast<const float4*>(&SA[wm * 64 + ms * 16 + g16 * 4]);
+        sv[ms][0] = s4.x; sv[ms][1] = s4.y; sv[ms][2] = s4.z; sv[ms][3] = s4.w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          c0[ms][i] = sv[i] * sw0;
-          c1[ms][i] = sv[i] * sw1;
-        }
+        for (int i = 0; i < 4; ++i) c[ms][i] = sv[ms][i] * sw0;
       }
       v8i af[4];
 #pragma unroll
@@ -285,6 +388,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) 
         af[ms] = v8i{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
                      (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
       }
+      v4f part[2][4];
 #pragma unroll
       for (int ns = 0; ns < 8; ++ns) {
         const int r = frag_row<SWIGLU>(wn, ns) + r16;
@@ -293,18 +397,35 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) 
         const v8i bf = v8i{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
                            (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-          const v4f part = mfma_fp8_16x16x128(af[ms], bf, v4f{0.f, 0.f, 0.f, 0.f});
+        for (int ms = 0; ms < 4; ++ms)
+          part[ns & 1][ms] = mfma_fp8_16x16x128(af[ms], bf, v4f{0.f, 0.f, 0.f, 0.f});
+        // promote the previous sub-tile column while this one is in the MFMA pipe
+        if (ns > 0) {
+          const int pn = ns - 1;
+          if (pn == 4) {   // sub-tiles 4..7 use the second weight-scale block
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[ms][ns][i] = fmaf(part[i], ns < 4 ? c0[ms][i] : c1[ms][i], acc[ms][ns][i]);
+            for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) c[ms][i] = sv[ms][i] * sw1;
+          }
+#pragma unroll
+          for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[ms][pn][i] = fmaf(part[pn & 1][ms][i], c[ms][i], acc[ms][pn][i]);
         }
       }
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[ms][7][i] = fmaf(part[1][ms][i], c[ms][i], acc[ms][7][i]);
     }
 
     // ---- epilogue at the end of a tile ----
     if (kb == KB - 1) {
-      unsigned char* E = smE[wave];
+      lds_barrier();   // every wave has finished reading slot st
+      unsigned char* E = sm + st * ST_BYTES + wave * 4096;
       if (SWIGLU) {
         // h = SiLU(g) * u; g in sub-tiles 0..3, u in 4..7 (same columns)
         float amax[4][4];
@@ -333,7 +454,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) 
             amax[ms][i] = v;
             if (r16 == 0) smAmax[wn][wm * 64 + ms * 16 + g16 * 4 + i] = v;
           }
-        __syncthreads();
+        lds_barrier();
         const int hcol0 = cur.n * 128 + wn * 64;
         const int nhs = p.f / 128;
 #pragma unroll
@@ -389,15 +510,15 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p) 
         for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-    if (!has_next) break;
-    commit_stage(st, tid, smA[buf ^ 1], smB[buf ^ 1], smSA[buf ^ 1]);
-    sw0 = st.sw0;
-    sw1 = st.sw1;
-    __syncthreads();
-    buf ^= 1;
-    kb = nkb;
-    L = nL;
-    cur = nxt;
+    // ---- next block ----
+    if (++kb == KB) {
+      kb = 0;
+      L += nslot;
+      if (L >= hi) break;
+      cur = decode_tile(p, offsets, smTile, NT, L);
+    }
+    next_issued = issued2;
+    st = (st + 1) % NSTAGE;
   }
 }
 
@@ -436,7 +557,7 @@ hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const 
   s1.f = f;
   s1.h = h;
   s1.hs = hs;
-  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(grid), dim3(G_THREADS), 0, stream, s1);
+  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(grid), dim3(G_THREADS), 0, stream, s1, offsets);
   return hipGetLastError();
 }
 
@@ -459,7 +580,7 @@ hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* of
   s2.bs = w2_s;
   s2.f = f;
   s2.y = y;
-  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(grid), dim3(G_THREADS), 0, stream, s2);
+  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(grid), dim3(G_THREADS), 0, stream, s2, offsets);
   return hipGetLastError();
 }
 
