@@ -17,7 +17,6 @@ dense FP8 MFMA peak, timed with HIP events on the stream it runs on;
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,25 +29,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import routing_fp8_grouped_amd as moe  # noqa: E402
-from routing_fp8_grouped_amd import configs, inputs  # noqa: E402
+from routing_fp8_grouped_amd import configs, inputs, profiling  # noqa: E402
 
 METRIC = "MoE-layer tokens/s at d=7168,E=256,k=8; FP8 grouped-GEMM % of MFMA peak"
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense E4M3 MFMA
 HBM_PEAK_GBS = 8000.0
 STAGES = ["route", "quant", "permute", "gemm_up", "gemm_down", "combine"]
-GEMM_SOURCES = ["routing_fp8_grouped_amd/csrc/gemm.hip", "routing_fp8_grouped_amd/csrc/common.h"]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
-
-def kernel_hash():
-    h = hashlib.sha256()
-    for p in GEMM_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def read_traffic(workload):
@@ -63,7 +53,7 @@ def read_traffic(workload):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_hash():
+    if vals.get("kernel_source_sha256_16") != profiling.gemm_source_hash():
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -99,12 +89,15 @@ def cpu_baseline(cfg, n_tokens):
     b = inputs.selection_bias(cfg).numpy()
     r = oroute.route(x, wg, b, cfg.G, cfg.M, cfg.k, cfg.route_scale)
     need = sorted(set(r["idx"].reshape(-1).tolist()) | {cfg.E})
-    host = {}
-    for e in need:
-        w13, w2 = inputs.expert_weights(cfg, e, "cuda")
-        host[e] = (w13.float().cpu().numpy(), w2.float().cpu().numpy())
-    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
-        q = dict(zip(need, ex.map(lambda e: olayer.quantize_expert(*host[e]), need)))
+
+    def quantize(e):
+        w13, w2 = inputs.expert_weights(cfg, e, "cuda")     # the GPU run's values
+        return olayer.quantize_expert(w13.float().cpu().numpy(), w2.float().cpu().numpy())
+
+    # at most `workers` experts in flight: ~1 GB of host memory each
+    workers = min(8, os.cpu_count() or 4)
+    with cf.ThreadPoolExecutor(workers) as ex:
+        q = dict(zip(need, ex.map(quantize, need)))
     t0 = time.perf_counter()
     olayer.moe_layer_tokens(x, wg, b, lambda e: q[e], cfg.G, cfg.M, cfg.k, cfg.route_scale)
     dt = time.perf_counter() - t0
@@ -122,7 +115,7 @@ def main():
     ap.add_argument("--workload", default="uniform_16k", choices=sorted(configs.CONFIGS))
     ap.add_argument("--dispatch", action="store_true",
                     help="copy the FP8 rows into grouped order instead of gathering in the GEMM")
-    ap.add_argument("--cpu-tokens", type=int, default=1)
+    ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
