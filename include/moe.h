@@ -141,7 +141,9 @@ moe_status moe_permute(const int32_t* idx, int T, int k, int E,
  *   w13 [n_groups, 2f, d] E4M3, w13_s [n_groups, 2f/128, d/128] FP32
  *   w2  [n_groups, d, f]  E4M3, w2_s  [n_groups, d/128, f/128]  FP32
  *   h, hs, y  outputs as above (h/hs are also the input of the second GEMM)
- * Row counts per group are read on the device: nothing waits on the host. */
+ * Row counts per group are read on the device: nothing waits on the host.
+ * MOE_ERR_UNSUPPORTED: n_groups > 1024, or 2f*d or total_rows*max(d, f) (or
+ * a_rows*d) above 2^32 bytes (the kernels use 32-bit byte offsets). */
 moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, int a_rows,
                                    const int32_t* row_src, const int32_t* offsets,
                                    int n_groups, int total_rows, int d, int f,

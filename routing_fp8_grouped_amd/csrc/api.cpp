@@ -185,13 +185,22 @@ moe_status check_gemm_shape(int n_groups, int total_rows, int d, int f) {
   REQUIRE(total_rows >= 0, "total_rows=%d is negative", total_rows);
   REQUIRE(d >= 128 && d % 128 == 0, "d=%d must be a positive multiple of 128", d);
   REQUIRE(f >= 128 && f % 128 == 0, "f=%d must be a positive multiple of 128", f);
+  // the kernels address one expert's weights and the activation rows with
+  // 32-bit byte offsets
+  if ((uint64_t)2 * f * d > 0xFFFFFFFFull)
+    return fail(MOE_ERR_UNSUPPORTED, "2f*d=%llu bytes per expert exceeds 4 GiB",
+                (unsigned long long)2 * f * d);
+  if ((uint64_t)total_rows * (uint64_t)(d > f ? d : f) > 0xFFFFFFFFull)
+    return fail(MOE_ERR_UNSUPPORTED, "total_rows*max(d,f) exceeds 4 GiB");
   return MOE_OK;
 }
 
-moe_status check_up(const uint8_t* aq, const float* as, int a_rows, const int32_t* row_src,
+moe_status check_up(int d, const uint8_t* aq, const float* as, int a_rows, const int32_t* row_src,
                     const int32_t* offsets, int total_rows, const uint8_t* w13, const float* w13_s,
                     uint8_t* h, float* hs) {
   REQUIRE(a_rows >= 1, "a_rows=%d must be >= 1", a_rows);
+  if ((uint64_t)a_rows * (uint64_t)d > 0xFFFFFFFFull)
+    return fail(MOE_ERR_UNSUPPORTED, "a_rows*d exceeds 4 GiB");
   REQUIRE(row_src != nullptr || a_rows >= total_rows,
           "a_rows=%d < total_rows=%d without row_src", a_rows, total_rows);
   REQUIRE_PTR(aq);
@@ -225,7 +234,7 @@ moe_status grouped_gemm_fp8_up(const uint8_t* aq, const float* as, int a_rows,
   clear_error();
   moe_status s = check_gemm_shape(n_groups, total_rows, d, f);
   if (s != MOE_OK || total_rows == 0) return s;
-  s = check_up(aq, as, a_rows, row_src, offsets, total_rows, w13, w13_s, h, hs);
+  s = check_up(d, aq, as, a_rows, row_src, offsets, total_rows, w13, w13_s, h, hs);
   if (s != MOE_OK) return s;
   return hip_status(moe::launch_gemm_up(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d,
                                         f, w13, w13_s, h, hs, static_cast<hipStream_t>(stream)),
@@ -253,7 +262,7 @@ moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, int a_row
   clear_error();
   moe_status s = check_gemm_shape(n_groups, total_rows, d, f);
   if (s != MOE_OK || total_rows == 0) return s;
-  s = check_up(aq, as, a_rows, row_src, offsets, total_rows, w13, w13_s, h, hs);
+  s = check_up(d, aq, as, a_rows, row_src, offsets, total_rows, w13, w13_s, h, hs);
   if (s != MOE_OK) return s;
   s = check_down(h, hs, offsets, w2, w2_s, y);
   if (s != MOE_OK) return s;

@@ -7,42 +7,50 @@
 //   stage 1  [rows, d] x W13[g]^T -> G, U  (K = d), epilogue h = SiLU(G) * U,
 //            1x128 requantisation of h -> E4M3 codes + FP32 scales
 //   stage 2  [rows, f] x W2[g]^T  -> Y     (K = f), epilogue BF16
-// Tiles are 128 rows x 256 weight rows; in stage 1 the 256 weight rows are the
+// Tiles are 256 rows x 256 weight rows; in stage 1 the 256 weight rows are the
 // 128 gate rows and the matching 128 up rows of one 128-wide slice of f, so one
-// tile yields one complete 1x128 tile of h.  K advances in 128-wide blocks, the
+// tile yields complete 1x128 tiles of h.  K advances in 128-wide blocks, the
 // granularity of both scales: one v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16
 // sub-tile computes the block's partial sum, which is promoted into the FP32
 // accumulator with the product of the row's activation scale and the weight
 // block's scale.  (The pages' H800 kernel promoted every four WGMMAs; on gfx950
 // a single MFMA spans exactly one scale block.)
 //
-// Work distribution: the tile list (group, n-tile, m-tile), m fastest, is built
-// on the device from the group offsets, so nothing waits on the host for the
-// ragged row counts.  Workgroup b runs on XCD b % 8 and takes the tiles of its
-// XCD's contiguous eighth of the list, so the workgroups sharing a weight tile
-// (consecutive m-tiles) run together behind one L2.
+// Per workgroup: 512 threads = 8 waves, two per SIMD, in a 4 x 2 grid.  Wave
+// (wm, wn) owns rows wm*64 .. +63 and weight-tile rows wn*128 .. +127 (in stage
+// 1: wn = 0 the gate rows, wn = 1 the up rows of the same h columns), i.e.
+// 4 x 8 MFMA sub-tiles and one weight scale block per K block.  With two waves
+// per SIMD the promotion FMAs of one wave issue while the other wave's MFMAs
+// run; within a wave each promotion trails its MFMA by two instructions.
 //
-// Per workgroup: 256 threads = 4 waves in a 2 x 2 grid, each wave 64 rows x 128
-// weight rows (4 x 8 MFMA sub-tiles).  Operands are double-buffered in LDS
-// (16-byte chunks XOR-swizzled by row); the next K block (possibly of the next
-// tile) is loaded into registers while the current one is multiplied.
+// Operands stream HBM -> LDS through a two-stage ring filled by direct
+// global->LDS loads (no VGPR round trip).  Each K block has one barrier, placed
+// after the wave's last LDS read of the block: past it the block's stage is
+// refilled with the block two ahead, and the first fragments of the next block
+// are read while the last MFMAs of this block run.
+//
+// Work distribution: the tile list (group, m super-block of 4 m-tiles, n-tile,
+// m-tile) is built on the device from the group offsets, so nothing waits on
+// the host for the ragged row counts.  Workgroup b runs on XCD b % 8 and takes
+// tiles of its XCD's contiguous eighth of the list, so the workgroups sharing a
+// weight tile or an activation tile run together behind one L2.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int GM = 128;   // rows per tile
-constexpr int GNB = 256;  // weight rows per tile
-constexpr int GK = 128;   // K block (scale block)
-constexpr int G_THREADS = 256;
-constexpr int G_MAX_GROUPS = 1024;
+constexpr int BM = 256;   // rows per tile
+constexpr int BN = 256;   // weight rows per tile
+constexpr int BK = 128;   // K block (scale block)
+constexpr int NTHR = 512;
+constexpr int MAX_GROUPS = 1024;
+constexpr int SUPER_M = 4;   // m-tiles per super-block of the tile order
 
 struct GemmArgs {
   const uint8_t* a;         // [a_rows, K] E4M3
   const float* as;          // [a_rows, K/128]
   int a_rows;
   const int32_t* row_src;   // [total rows] source row of each row, or null (identity)
-  const int32_t* offsets;   // [n_groups + 1]
   int n_groups;
   int total_rows;           // rows of h / y (and of row_src)
   int K;
@@ -59,11 +67,17 @@ struct GemmArgs {
 // LDS layout of a 128-byte operand row r: its 16-byte chunk c sits at chunk
 // position c ^ swz(r).  A fragment read (ds_read_b128) has lanes 0..15 on rows
 // r0..r0+15 at one chunk; swz gives rows r0..r0+7 eight different positions
-// (conflict-free when 8 lanes are served per cycle) and gives the even rows
-// and the odd rows of r0..r0+15 eight positions each (conflict-free when 16
-// lanes are served per cycle over 64 banks).
+// and gives the even rows and the odd rows of r0..r0+15 eight positions each,
+// so the read is conflict-free whether 8 or 16 lanes are served per cycle.
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
-__device__ __forceinline__ int op_off(int r, int c) { return r * GK + ((c ^ swz(r)) << 4); }
+__device__ __forceinline__ int op_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 4); }
+
+// ---- LDS ring: two K blocks, filled by direct global->LDS loads ----
+constexpr int ST_A = BM * BK;                   // activation tile, 32 KB
+constexpr int ST_B = BN * BK;                   // weight tile, 32 KB
+constexpr int ST_SA = BM * 4;                   // activation scales of the 256 rows
+constexpr int ST_SW = 256;                      // weight scales: [0] wave column 0, [1] column 1
+constexpr int STG = ST_A + ST_B + ST_SA + ST_SW;
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -71,42 +85,14 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-struct Tile {
-  int g, n, row0, rows_valid;
-};
-
-// Weight row (within the group) held by row rr of the LDS weight tile.
-template <bool SWIGLU>
-__device__ __forceinline__ int weight_row(const GemmArgs& p, int n, int rr) {
-  if (SWIGLU) return rr < 128 ? n * 128 + rr : p.f + n * 128 + (rr - 128);
-  return n * GNB + rr;
-}
-
-// LDS weight-tile row of sub-tile ns for wave column wn.
-template <bool SWIGLU>
-__device__ __forceinline__ int frag_row(int wn, int ns) {
-  if (SWIGLU) return ns < 4 ? wn * 64 + ns * 16 : 128 + wn * 64 + (ns - 4) * 16;
-  return wn * 128 + ns * 16;
-}
-
-// ---- LDS ring: NSTAGE K blocks in flight, filled by direct global->LDS loads ----
-constexpr int NSTAGE = 3;
-constexpr int ST_A = GM * GK;                   // activation tile, 16 KB
-constexpr int ST_B = GNB * GK;                  // weight tile, 32 KB
-constexpr int ST_SA = 256 * 4;                  // activation scales (rows 0..127; 128..255 spare)
-constexpr int ST_SW = 4 * 256;                  // per wave: its two weight-block scales
-constexpr int ST_BYTES = ST_A + ST_B + ST_SA + ST_SW;
-// DMA instructions per wave per K block: 4 (A) + 8 (B) + 1 (SA) + 1 (SW).
-constexpr int DMA_PER_STAGE = 14;
-
 // Direct global->LDS loads.  Lane l of the wave writes its 16 (or 4) bytes at
 // LDS byte address lds + 16 l (4 l); the source address is per lane.  They are
 // issued from inline assembly so that the compiler does not track them: it
 // would otherwise make every later LDS read wait for all of them, which would
 // drain the pipeline each K block.  The instructions have no register outputs
 // (the data goes to LDS); every LDS read of their data follows an explicit
-// vmcnt wait and a barrier below, and every reuse of a ring slot follows a
-// barrier.  M0 carries the LDS address; the compiler does not allocate it.
+// vmcnt wait and a barrier, and every reuse of a ring slot follows a barrier.
+// M0 carries the LDS address; the compiler does not allocate it.
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -129,13 +115,28 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | (((N >> 4) & 3) << 14));
+// Wait for all of this wave's LDS reads and direct loads, then barrier.  The
+// barrier is written in assembly with a memory clobber so that the compiler
+// moves no LDS access across it.
+__device__ __forceinline__ void ring_barrier() {
+  // gfx9 s_waitcnt fields: vmcnt[3:0] bits 3:0, expcnt 6:4, lgkmcnt 11:8,
+  // vmcnt[5:4] bits 15:14
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0), expcnt unconstrained
+  asm volatile("s_barrier" ::: "memory");
+}
+// Barrier for LDS data only: waits for this wave's LDS operations, not for the
+// direct loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
+  asm volatile("s_barrier" ::: "memory");
 }
 
+struct Tile {
+  int g, n, row0, rows_valid;
+};
+
+// Tile l of the list: groups in order; inside a group, super-blocks of
+// SUPER_M m-tiles; inside a super-block n-tiles, and m-tiles fastest.
 __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* __restrict__ offsets,
                                             const int* smTile, int NT, long l) {
   const int q = (int)(l / NT);
@@ -145,133 +146,364 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* __
     if (smTile[mid] <= q) a = mid; else b = mid - 1;
   }
   a = __builtin_amdgcn_readfirstlane(a);   // uniform: offsets come through scalar loads
+  const int mt = __builtin_amdgcn_readfirstlane(smTile[a + 1] - smTile[a]);
+  const int local = (int)(l - (long)smTile[a] * NT);
+  const int sb = local / (SUPER_M * NT);
+  const int rem = local - sb * SUPER_M * NT;
+  const int msb = min(SUPER_M, mt - sb * SUPER_M);
   Tile t;
   t.g = a;
-  const int mtg = __builtin_amdgcn_readfirstlane(smTile[a + 1] - smTile[a]);
-  const int local = (int)(l - (long)smTile[a] * NT);
-  t.n = local / mtg;
-  const int m = local - t.n * mtg;
-  t.row0 = offsets[a] + m * GM;
+  t.n = rem / msb;
+  const int m = sb * SUPER_M + (rem - t.n * msb);
+  t.row0 = offsets[a] + m * BM;
   // rows past total_rows (only possible with malformed offsets) are never touched
-  t.rows_valid = min(GM, min(offsets[a + 1], p.total_rows) - t.row0);
+  t.rows_valid = min(BM, min(offsets[a + 1], p.total_rows) - t.row0);
   return t;
 }
 
-// Per-lane global sources of one wave's DMA instructions for a tile; the K block
-// offset is added at issue time.  LDS destinations are fixed: instruction i of
-// wave w writes 1 KB at (w * n_i + i) KB of its region, lane l 16 bytes at
-// 16 l, i.e. row 8 (w * n_i + i) + l / 8, physical chunk l % 8, which holds the
-// logical chunk (l % 8) ^ swz(row) (the swizzle is applied on the
-// source side).
-struct TileSrc {
-  uint32_t a[4];          // byte offsets into p.a
-  uint32_t b[8];          // byte offsets into the group's weights
-  uint32_t sa;            // byte offset into p.as
-  uint32_t sw;            // byte offset into p.bs
-  const uint8_t* bbase;   // the group's weights (uniform)
-};
-
-// Source rows (in p.a) of this lane's 4 activation DMA rows and its scale row.
-struct TileRows {
-  int a[4];
-  int sa;
-};
-
-// Row of p.a holding tile row r (rows past the group's end repeat its last row).
+// Row of p.a's row space holding tile row r (rows past the group's end repeat
+// its last row; they are multiplied but never stored).
 __device__ __forceinline__ int tile_row(const GemmArgs& p, const Tile& t, int r) {
   return min(max(t.row0 + min(r, t.rows_valid - 1), 0), p.total_rows - 1);
 }
 
-// Gather indices of a tile's 128 rows, DMA'd into an LDS table one tile ahead
-// (lane l of wave w fetches row_src of tile row (w & 1) * 64 + l; waves 2 and 3
-// repeat waves 0 and 1), so no register ever waits on them.
-__device__ __forceinline__ void dma_tile_rows(const GemmArgs& p, const Tile& t, int wave, int lane,
-                                              unsigned char* table) {
-  const int r = (wave & 1) * 64 + lane;
-  dma4(p.row_src, (uint32_t)tile_row(p, t, r) * 4u, lds_addr(table + (wave & 1) * 256));
+// Per-lane global sources of one wave's direct loads for a tile, kept in LDS
+// (9 words per lane: [0..3] activation rows, [4..7] weight rows, [8] a scale
+// row) so that no register holds them across the multiply; the K block offset
+// is added at issue time.  Instruction i of wave w writes 1 KB at (4 w + i) KB
+// of its operand region: lane l writes 16 bytes at 16 l, i.e. tile row
+// 8 (4 w + i) + l / 8, physical chunk l % 8, which holds the logical chunk
+// (l % 8) ^ swz(row) (the swizzle is applied on the source side).  Waves 0..3
+// also load the activation scales of rows 64 w .. 64 w + 63 (word 8 is a byte
+// offset into p.as), wave 4 the weight scales (word 8 is a byte offset into
+// p.bs; lane parity selects the scale block of wave column 0 or 1).
+constexpr int SRC_WORDS = 9;
+
+// Weight row (within the group) held by row rr of the LDS weight tile.
+template <bool SWIGLU>
+__device__ __forceinline__ int weight_row(const GemmArgs& p, int n, int rr) {
+  if (SWIGLU) return rr < 128 ? n * 128 + rr : p.f + n * 128 + (rr - 128);
+  return n * BN + rr;
 }
 
-__device__ __forceinline__ TileRows tile_rows(const GemmArgs& p, const Tile& t, const int* table,
-                                              int wave, int lane) {
-  TileRows r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = (wave * 4 + i) * 8 + (lane >> 3);
-    r.a[i] = p.row_src ? table[rr] : tile_row(p, t, rr);
+// Gather indices of a tile's 256 rows, loaded into an LDS table one tile ahead
+// (waves 0..3, lane l: tile row 64 w + l), so no register waits on them.
+__device__ __forceinline__ void dma_tile_rows(const GemmArgs& p, const Tile& t, int wave, int lane,
+                                              int* table) {
+  if (wave < 4) {
+    const int r = wave * 64 + lane;
+    dma4(p.row_src, (uint32_t)tile_row(p, t, r) * 4u, lds_addr(table + wave * 64));
   }
-  const int rs = (wave & 1) * 64 + lane;
-  r.sa = p.row_src ? table[rs] : tile_row(p, t, rs);
-  return r;
 }
 
 template <bool SWIGLU>
-__device__ __forceinline__ TileSrc tile_sources(const GemmArgs& p, const Tile& t, const TileRows& rows,
-                                                int wave, int lane) {
-  TileSrc s;
-  const int KS = p.K / GK;
+__device__ __forceinline__ void build_sources(const GemmArgs& p, const Tile& t, const int* table,
+                                              int wave, int lane, uint32_t* srcw) {
+  const int KS = p.K / BK;
   const int pc = lane & 7;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (wave * 4 + i) * 8 + (lane >> 3);
     const int c = pc ^ swz(r);
-    const int row = min(max(rows.a[i], 0), p.a_rows - 1);
-    s.a[i] = (uint32_t)row * (uint32_t)p.K + c * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rr = (wave * 8 + i) * 8 + (lane >> 3);
-    const int c = pc ^ swz(rr);
-    int wr = weight_row<SWIGLU>(p, t.n, rr);
+    int row = p.row_src ? table[r] : tile_row(p, t, r);
+    row = min(max(row, 0), p.a_rows - 1);
+    srcw[i * 64 + lane] = (uint32_t)row * (uint32_t)p.K + c * 16;
+    int wr = weight_row<SWIGLU>(p, t.n, r);
     if (wr >= p.N) wr = 0;   // padding rows of a partial tile: any valid row, never stored
-    s.b[i] = (uint32_t)wr * (uint32_t)p.K + c * 16;
+    srcw[(4 + i) * 64 + lane] = (uint32_t)wr * (uint32_t)p.K + c * 16;
   }
-  s.bbase = p.b + (size_t)t.g * p.N * p.K;
-  s.sa = (uint32_t)min(max(rows.sa, 0), p.a_rows - 1) * (uint32_t)(KS * 4);
-  {
-    // even lanes: this wave's first weight-scale block, odd lanes: its second
+  uint32_t so;
+  if (wave < 4) {
+    const int rs = wave * 64 + lane;
+    int row = p.row_src ? table[rs] : tile_row(p, t, rs);
+    row = min(max(row, 0), p.a_rows - 1);
+    so = (uint32_t)row * (uint32_t)(KS * 4);
+  } else {
     const int nsb = p.N / 128;
-    const int wn = wave & 1;
     int sb;
     if (SWIGLU) sb = (lane & 1) ? p.f / 128 + t.n : t.n;
-    else sb = min(2 * t.n + wn, nsb - 1);
-    s.sw = (uint32_t)(t.g * nsb + sb) * (uint32_t)(KS * 4);
+    else sb = min(2 * t.n + (lane & 1), nsb - 1);
+    so = (uint32_t)(t.g * nsb + sb) * (uint32_t)(KS * 4);
   }
-  return s;
+  srcw[8 * 64 + lane] = so;
 }
 
-__device__ __forceinline__ void issue_stage(const GemmArgs& p, const TileSrc& s, int kb, int wave,
-                                            unsigned char* stage) {
+__device__ __forceinline__ void issue_stage(const GemmArgs& p, const uint8_t* bbase, const uint32_t* srcw,
+                                            int kb, int wave, int lane, unsigned char* stage) {
   const uint32_t base = lds_addr(stage);
-  const uint8_t* a = p.a + (size_t)kb * GK;
-  const uint8_t* b = s.bbase + (size_t)kb * GK;
+  const uint8_t* a = p.a + (size_t)kb * BK;
+  const uint8_t* b = bbase + (size_t)kb * BK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(a, s.a[i], base + (wave * 4 + i) * 1024);
+  for (int i = 0; i < 4; ++i) dma16(a, srcw[i * 64 + lane], base + (wave * 4 + i) * 1024);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dma16(b, s.b[i], base + ST_A + (wave * 8 + i) * 1024);
-  dma4(p.as + kb, s.sa, base + ST_A + ST_B + (wave & 1) * 256);
-  dma4(p.bs + kb, s.sw, base + ST_A + ST_B + ST_SA + wave * 256);
+  for (int i = 0; i < 4; ++i) dma16(b, srcw[(4 + i) * 64 + lane], base + ST_A + (wave * 4 + i) * 1024);
+  if (wave < 4) dma4(p.as + kb, srcw[8 * 64 + lane], base + ST_A + ST_B + wave * 256);
+  else if (wave == 4) dma4(p.bs + kb, srcw[8 * 64 + lane], base + ST_A + ST_B + ST_SA);
 }
 
-// Barrier for LDS data only: waits for this wave's LDS operations, not for the
-// DMA loads in flight (a __syncthreads() fence would drain those too).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
-  __builtin_amdgcn_s_barrier();
+// MFMA operand fragment: rows r (this lane's row r16 added by the caller),
+// K bytes [g16 * 32, g16 * 32 + 32).
+__device__ __forceinline__ v8i frag(const unsigned char* T, int r, int g16) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(T + op_off(r, g16 * 2));
+  const uint4 hi = *reinterpret_cast<const uint4*>(T + op_off(r, g16 * 2 + 1));
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// SiLU(g) * u in FP32.
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// ---- epilogues: one 64 x 128 block per wave, written through the wave's own
+// part of the finished ring stage E, 32 rows per round ----
+
+// Stage 1.  Wave (wm, 0) holds g, wave (wm, 1) holds u for the same 64 x 128
+// block of h.  Column WN finishes h columns 64 WN .. 64 WN + 63: it sends the
+// other half to its partner and receives the partner's half of its own.  h
+// replaces g (WN = 0) or u (WN = 1) in the accumulator.  Then the 1x128 amax
+// is combined across the pair through smAmax, and the E4M3 codes are staged
+// for 16-byte stores.
+template <int WN>
+__device__ __forceinline__ void epilogue_swiglu(const GemmArgs& p, const Tile& cur, v4f (&acc)[4][8],
+                                                unsigned char* E, float (*smAmax)[BM], int wave,
+                                                int wm, int lane) {
+  const int g16 = lane >> 4, r16 = lane & 15;
+  float* X = reinterpret_cast<float*>(E);
+  float* mine = X + wave * 2048;
+  const float* other = X + (wave ^ 1) * 2048;
+  const int nhs = p.f / 128;
+  constexpr int SEND = WN == 0 ? 4 : 0;   // sub-tile columns sent to the partner
+  constexpr int KEEP = WN == 0 ? 0 : 4;   // sub-tile columns finished here
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int msl = 0; msl < 2; ++msl)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          mine[((msl * 4 + j) * 4 + e) * 64 + lane] = acc[2 * r + msl][SEND + j][e];
+    lds_barrier();
+    float amax[2][4];
+#pragma unroll
+    for (int msl = 0; msl < 2; ++msl) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax[msl][e] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = other[((msl * 4 + j) * 4 + e) * 64 + lane];
+          const float mv = acc[2 * r + msl][KEEP + j][e];
+          const float h = WN == 0 ? swiglu(mv, v) : swiglu(v, mv);
+          acc[2 * r + msl][KEEP + j][e] = h;
+          amax[msl][e] = fmaxf(amax[msl][e], fabsf(h));
+        }
+    }
+#pragma unroll
+    for (int msl = 0; msl < 2; ++msl)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = amax[msl][e];
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+        if (r16 == 0) smAmax[WN][wm * 64 + (2 * r + msl) * 16 + g16 * 4 + e] = v;
+      }
+    lds_barrier();   // amax of both halves visible; the partner is done with `mine`
+    unsigned char* Q = reinterpret_cast<unsigned char*>(mine);   // 32 rows x 64 bytes
+#pragma unroll
+    for (int msl = 0; msl < 2; ++msl)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rt = wm * 64 + (2 * r + msl) * 16 + g16 * 4 + e;
+        const float sc = scale_from_amax(fmaxf(smAmax[0][rt], smAmax[1][rt]));
+        if (WN == 0 && r16 == 0 && rt < cur.rows_valid) p.hs[(size_t)(cur.row0 + rt) * nhs + cur.n] = sc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t q = f32x2_to_e4m3(acc[2 * r + msl][KEEP + j][e] / sc, 0.0f) & 0xFFu;
+          Q[(msl * 16 + g16 * 4 + e) * 64 + j * 16 + r16] = (unsigned char)q;
+        }
+      }
+    wave_sync_lds();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int idx = it * 64 + lane;
+      const int rl = idx >> 2, cq = idx & 3;
+      const int rt = wm * 64 + 2 * r * 16 + rl;
+      const uint4 v = *reinterpret_cast<const uint4*>(Q + rl * 64 + cq * 16);
+      if (rt < cur.rows_valid)
+        *reinterpret_cast<uint4*>(p.h + (size_t)(cur.row0 + rt) * p.f + cur.n * 128 + WN * 64 + cq * 16) = v;
+    }
+    wave_sync_lds();
+  }
+}
+
+// Stage 2: BF16 rows, 32 rows x 128 columns per round.
+__device__ __forceinline__ void epilogue_bf16(const GemmArgs& p, const Tile& cur, v4f (&acc)[4][8],
+                                              unsigned char* E, int wave, int wm, int wn, int lane) {
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int col0 = cur.n * BN + wn * 128;
+  if (col0 >= p.N) return;
+  uint16_t* X16 = reinterpret_cast<uint16_t*>(E) + wave * 4096;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int msl = 0; msl < 2; ++msl)
+#pragma unroll
+      for (int ns = 0; ns < 8; ++ns)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          X16[(msl * 16 + g16 * 4 + e) * 128 + ns * 16 + r16] = f32_to_bf16(acc[2 * r + msl][ns][e]);
+    wave_sync_lds();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int idx = it * 64 + lane;
+      const int rl = idx >> 4, cq = idx & 15;
+      const int rt = wm * 64 + 2 * r * 16 + rl;
+      const uint4 v = *reinterpret_cast<const uint4*>(X16 + rl * 128 + cq * 8);
+      if (rt < cur.rows_valid)
+        *reinterpret_cast<uint4*>(p.y + (size_t)(cur.row0 + rt) * p.N + col0 + cq * 8) = v;
+    }
+    wave_sync_lds();
+  }
+}
+
+// Loader: issues the K blocks of this workgroup's tiles into the ring, one
+// block per call.  When it starts a tile it builds the tile's sources from the
+// gather table and loads the gather indices of its next tile into the other
+// table; every ring barrier waits for all direct loads, so those land before
+// they are used.
+template <bool SWIGLU>
+struct Loader {
+  const GemmArgs& p;
+  const int32_t* __restrict__ offsets;
+  const int* smTile;
+  int (*smRows)[BM];
+  int NT, KB, wave, lane, nslot;
+  long hi;
+  long L;
+  int kb, par;
+  bool more;
+  uint32_t* srcw;          // this wave's source table in LDS
+  Tile tile;
+  const uint8_t* bbase;    // the loader tile's group weights (uniform)
+
+  __device__ __forceinline__ void issue(unsigned char* stage) {
+    if (kb == 0) {
+      build_sources<SWIGLU>(p, tile, smRows[par], wave, lane, srcw);
+      bbase = p.b + (size_t)tile.g * p.N * p.K;
+      if (p.row_src && L + nslot < hi)
+        dma_tile_rows(p, decode_tile(p, offsets, smTile, NT, L + nslot), wave, lane, smRows[par ^ 1]);
+    }
+    issue_stage(p, bbase, srcw, kb, wave, lane, stage);
+    if (++kb == KB) {
+      kb = 0;
+      L += nslot;
+      par ^= 1;
+      more = L < hi;
+      if (more) tile = decode_tile(p, offsets, smTile, NT, L);
+    }
+  }
+};
+
+// Per-wave register state of the multiply.
+struct Frags {
+  v8i af[4];       // activation fragments of the block (rows ms*16 .. +15)
+  v8i bq[2];       // weight fragments, column ns in slot ns & 1
+  float cs[4][4];  // activation scale x weight scale of this lane's 16 rows
+};
+
+__device__ __forceinline__ void load_scales(Frags& F, const unsigned char* stage, int wm, int wn, int g16) {
+  const unsigned char* B_ = stage + ST_A;
+  const float* SA_ = reinterpret_cast<const float*>(B_ + ST_B);
+  const float sw = reinterpret_cast<const float*>(B_ + ST_B + ST_SA)[wn];
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+    const float4 s4 = *reinterpret_cast<const float4*>(&SA_[wm * 64 + ms * 16 + g16 * 4]);
+    F.cs[ms][0] = s4.x * sw;
+    F.cs[ms][1] = s4.y * sw;
+    F.cs[ms][2] = s4.z * sw;
+    F.cs[ms][3] = s4.w * sw;
+  }
+}
+
+__device__ __forceinline__ void load_first(Frags& F, const unsigned char* stage, int wm, int wn, int g16,
+                                           int r16) {
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) F.af[ms] = frag(stage, wm * 64 + ms * 16 + r16, g16);
+  F.bq[0] = frag(stage + ST_A, wn * 128 + r16, g16);
+  load_scales(F, stage, wm, wn, g16);
+}
+
+// One K block on stage `cur`: MFMA i = (ns, ms) in ns-major order, each
+// partial promoted after the next MFMA has been issued; the weight fragment of
+// column ns + 1 is read while column ns is multiplied.  After the last read of
+// `cur` (column 7's fragment) comes the ring barrier; unless LAST, the stage
+// is then refilled (the loader's next block) and the first fragments of the
+// next block are read from `nxt` while column 7 is multiplied.
+template <bool SWIGLU, bool LAST>
+__device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGLU>& ld,
+                                        unsigned char* cur, const unsigned char* nxt, int wm, int wn,
+                                        int g16, int r16) {
+  const unsigned char* Bc = cur + ST_A;
+  v4f part[2];
+#pragma unroll
+  for (int ns = 0; ns < 8; ++ns) {
+    // the register budget holds two weight fragments: no LDS read moves across
+    // columns (an empty asm with a memory clobber pins them in order)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (ns < 7) F.bq[(ns + 1) & 1] = frag(Bc, wn * 128 + (ns + 1) * 16 + r16, g16);
+    if (ns == 7) {
+      ring_barrier();
+      if (!LAST) {
+        if (ld.more) ld.issue(cur);
+        F.bq[0] = frag(nxt + ST_A, wn * 128 + r16, g16);
+      }
+    }
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+      const int i = ns * 4 + ms;
+      part[i & 1] = mfma_fp8_16x16x128(F.af[ms], F.bq[ns & 1], v4f{0.f, 0.f, 0.f, 0.f});
+      if (i >= 1) {
+        const int pi = i - 1, pms = pi & 3, pns = pi >> 2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[pms][pns][e] = fmaf(part[pi & 1][e], F.cs[pms][e], acc[pms][pns][e]);
+        // pins the promotion (and so the MFMAs before it) at this point: the
+        // compiler would otherwise sink the block's arithmetic past the ring
+        // barrier and hold every weight fragment at once
+        asm volatile("" : "+v"(acc[pms][pns]));
+      }
+      if (ns == 7 && !LAST) {
+        // the next block's fragment ms replaces this one once its last MFMA is issued
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        F.af[ms] = frag(nxt, wm * 64 + ms * 16 + r16, g16);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[3][7][e] = fmaf(part[1][e], F.cs[3][e], acc[3][7][e]);
+  if (!LAST) load_scales(F, nxt, wm, wn, g16);
 }
 
 template <bool SWIGLU>
-__global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p,
-                                                                    const int32_t* __restrict__ offsets) {
-  __shared__ __attribute__((aligned(16))) unsigned char sm[NSTAGE * ST_BYTES];
-  __shared__ float smAmax[2][GM];
-  __shared__ int smTile[G_MAX_GROUPS + 1];
-  __shared__ __attribute__((aligned(16))) int smRows[2][GM];   // gather indices, by tile parity
+__global__ __launch_bounds__(NTHR, 1) void grouped_gemm_kernel(GemmArgs p,
+                                                              const int32_t* __restrict__ offsets) {
+  __shared__ __attribute__((aligned(16))) unsigned char sm[2 * STG];
+  __shared__ int smTile[MAX_GROUPS + 1];
+  __shared__ __attribute__((aligned(16))) int smRows[2][BM];   // gather indices, by tile parity
+  __shared__ float smAmax[2][BM];
+  __shared__ uint32_t smSrc[NTHR / 64][SRC_WORDS * 64];   // per-wave source tables
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int g16 = lane >> 4, r16 = lane & 15;
-  const int KB = p.K / GK;
+  const int KB = p.K / BK;
   const int NT = p.n_tiles_n;
 
   // ---- tile list: m-tiles per group, exclusive prefix in LDS ----
@@ -280,7 +512,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p,
     for (int base = 0; base < p.n_groups; base += 64) {
       const int g = base + lane;
       int mt = 0;
-      if (g < p.n_groups) mt = (offsets[g + 1] - offsets[g] + GM - 1) / GM;
+      if (g < p.n_groups) mt = (offsets[g + 1] - offsets[g] + BM - 1) / BM;
       int v = mt;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -300,225 +532,49 @@ __global__ __launch_bounds__(G_THREADS, 1) void grouped_gemm_kernel(GemmArgs p,
   const long lo = total * xcd / 8, hi = total * (xcd + 1) / 8;
   if (lo + slot >= hi) return;
 
-  // Loader state runs up to two K blocks ahead of the multiply.  When it starts
-  // a tile it builds the tile's DMA sources from the gather table and DMAs the
-  // gather indices of its next tile into the other table; those land before the
-  // next tile starts (every wait below covers all DMAs older than the block
-  // about to be multiplied, and the barrier publishes them to all waves).
-  long ld_L = lo + slot;
-  int ld_kb = 0;
-  int ld_par = 0;
-  bool ld_more = true;   // is there a (tile, K block) at the loader position?
-  Tile ld_tile = decode_tile(p, offsets, smTile, NT, ld_L);
-  TileSrc src;
+  Loader<SWIGLU> ld{p, offsets, smTile, smRows, NT, KB, wave, lane, nslot, hi, lo + slot, 0, 0, true,
+                    smSrc[wave]};
+  ld.tile = decode_tile(p, offsets, smTile, NT, ld.L);
   if (p.row_src) {
-    dma_tile_rows(p, ld_tile, wave, lane, reinterpret_cast<unsigned char*>(smRows[0]));
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
+    dma_tile_rows(p, ld.tile, wave, lane, smRows[0]);
+    ring_barrier();
   }
-#define LOADER_ISSUE(dst)                                                              \
-  do {                                                                                 \
-    if (ld_kb == 0) {                                                                  \
-      src = tile_sources<SWIGLU>(p, ld_tile, tile_rows(p, ld_tile, smRows[ld_par], wave, lane), \
-                                 wave, lane);                                          \
-      if (p.row_src && ld_L + nslot < hi)                                              \
-        dma_tile_rows(p, decode_tile(p, offsets, smTile, NT, ld_L + nslot), wave, lane,         \
-                      reinterpret_cast<unsigned char*>(smRows[ld_par ^ 1]));           \
-    }                                                                                  \
-    issue_stage(p, src, ld_kb, wave, (dst));                                              \
-    if (++ld_kb == KB) {                                                               \
-      ld_kb = 0;                                                                       \
-      ld_L += nslot;                                                                   \
-      ld_par ^= 1;                                                                     \
-      ld_more = ld_L < hi;                                                             \
-      if (ld_more) ld_tile = decode_tile(p, offsets, smTile, NT, ld_L);                         \
-    }                                                                                  \
-  } while (0)
+  // prologue: blocks 0 and 1 in flight, block 0 landed
+  ld.issue(sm);
+  ring_barrier();
+  if (ld.more) ld.issue(sm + STG);
 
-  // prologue: blocks 0 and 1 in flight
-  LOADER_ISSUE(sm);
-  bool next_issued = false;
-  if (ld_more) {
-    LOADER_ISSUE(sm + ST_BYTES);
-    next_issued = true;
-  }
-
-  v4f acc[4][8];
+  Frags F;
+  load_first(F, sm, wm, wn, g16, r16);
+  int S = 0;   // ring stage of the block being multiplied
+  for (long L = lo + slot; L < hi; L += nslot) {
+    const Tile cur = decode_tile(p, offsets, smTile, NT, L);
+    v4f acc[4][8];
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms)
+    for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-    for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  long L = lo + slot;
-  Tile cur = decode_tile(p, offsets, smTile, NT, L);
-  int kb = 0;
-  int st = 0;   // ring slot of the block being multiplied
-
-  while (true) {
-    // block `st` has landed once at most the next block's DMAs are outstanding
-    if (next_issued) wait_vmcnt<DMA_PER_STAGE>(); else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();   // all lanes' DMAs visible; slot st+2 free again
-    bool issued2 = false;
-    if (ld_more) {
-      LOADER_ISSUE(sm + ((st + 2) % NSTAGE) * ST_BYTES);
-      issued2 = true;
+      for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < KB - 1; ++kb) {
+      k_block<SWIGLU, false>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16);
+      S ^= 1;
     }
+    k_block<SWIGLU, true>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16);
 
-    // ---- multiply block `st` ----
-    {
-      const unsigned char* A = sm + st * ST_BYTES;
-      const unsigned char* B = A + ST_A;
-      const float* SA = reinterpret_cast<const float*>(B + ST_B);
-      const float* SW = reinterpret_cast<const float*>(B + ST_B + ST_SA + wave * 256);
-      const float sw0 = SW[0], sw1 = SW[1];
-      float sv[4][4], c[4][4];
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        const float4 s4 = *reinterpret_cast<const float4*>(&SA[wm * 64 + ms * 16 + g16 * 4]);
-        sv[ms][0] = s4.x; sv[ms][1] = s4.y; sv[ms][2] = s4.z; sv[ms][3] = s4.w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c[ms][i] = sv[ms][i] * sw0;
-      }
-      v8i af[4];
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        const int r = wm * 64 + ms * 16 + r16;
-        const uint4 lo4 = *reinterpret_cast<const uint4*>(A + op_off(r, g16 * 2));
-        const uint4 hi4 = *reinterpret_cast<const uint4*>(A + op_off(r, g16 * 2 + 1));
-        af[ms] = v8i{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
-                     (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
-      }
-      v4f part[2][4];
-#pragma unroll
-      for (int ns = 0; ns < 8; ++ns) {
-        const int r = frag_row<SWIGLU>(wn, ns) + r16;
-        const uint4 lo4 = *reinterpret_cast<const uint4*>(B + op_off(r, g16 * 2));
-        const uint4 hi4 = *reinterpret_cast<const uint4*>(B + op_off(r, g16 * 2 + 1));
-        const v8i bf = v8i{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
-                           (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-          part[ns & 1][ms] = mfma_fp8_16x16x128(af[ms], bf, v4f{0.f, 0.f, 0.f, 0.f});
-        // promote the previous sub-tile column while this one is in the MFMA pipe
-        if (ns > 0) {
-          const int pn = ns - 1;
-          if (pn == 4) {   // sub-tiles 4..7 use the second weight-scale block
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) c[ms][i] = sv[ms][i] * sw1;
-          }
-#pragma unroll
-          for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[ms][pn][i] = fmaf(part[pn & 1][ms][i], c[ms][i], acc[ms][pn][i]);
-        }
-      }
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[ms][7][i] = fmaf(part[1][ms][i], c[ms][i], acc[ms][7][i]);
+    // ---- epilogue, through stage S (every wave has finished reading it: the
+    // ring barrier of the last block followed the last read) ----
+    unsigned char* E = sm + S * STG;
+    if (SWIGLU) {
+      if (wn == 0) epilogue_swiglu<0>(p, cur, acc, E, smAmax, wave, wm, lane);
+      else epilogue_swiglu<1>(p, cur, acc, E, smAmax, wave, wm, lane);
+    } else {
+      epilogue_bf16(p, cur, acc, E, wave, wm, wn, lane);
     }
-
-    // ---- epilogue at the end of a tile ----
-    if (kb == KB - 1) {
-      lds_barrier();   // every wave has finished reading slot st
-      unsigned char* E = sm + st * ST_BYTES + wave * 4096;
-      if (SWIGLU) {
-        // h = SiLU(g) * u; g in sub-tiles 0..3, u in 4..7 (same columns)
-        float amax[4][4];
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) amax[ms][i] = 0.0f;
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float gv = acc[ms][c][i], uv = acc[ms][4 + c][i];
-              const float hv = gv / (1.0f + expf(-gv)) * uv;
-              acc[ms][c][i] = hv;
-              amax[ms][i] = fmaxf(amax[ms][i], fabsf(hv));
-            }
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = amax[ms][i];
-#pragma unroll
-            for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-            amax[ms][i] = v;
-            if (r16 == 0) smAmax[wn][wm * 64 + ms * 16 + g16 * 4 + i] = v;
-          }
-        lds_barrier();
-        const int hcol0 = cur.n * 128 + wn * 64;
-        const int nhs = p.f / 128;
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-          float sc[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rt = wm * 64 + ms * 16 + g16 * 4 + i;
-            sc[i] = scale_from_amax(fmaxf(smAmax[0][rt], smAmax[1][rt]));
-            if (wn == 0 && r16 == 0 && rt < cur.rows_valid)
-              p.hs[(size_t)(cur.row0 + rt) * nhs + cur.n] = sc[i];
-          }
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t q = f32x2_to_e4m3(acc[ms][c][i] / sc[i], 0.0f) & 0xFFu;
-              E[(g16 * 4 + i) * 64 + c * 16 + r16] = (unsigned char)q;
-            }
-          wave_sync_lds();
-          const int rl = lane >> 2, cq = lane & 3;
-          const int rt = wm * 64 + ms * 16 + rl;
-          const uint4 v = *reinterpret_cast<const uint4*>(E + rl * 64 + cq * 16);
-          if (rt < cur.rows_valid)
-            *reinterpret_cast<uint4*>(p.h + (size_t)(cur.row0 + rt) * p.f + hcol0 + cq * 16) = v;
-          wave_sync_lds();
-        }
-      } else {
-        const int col0 = cur.n * GNB + wn * 128;
-        const bool col_ok = col0 < p.N;
-        uint16_t* E16 = reinterpret_cast<uint16_t*>(E);
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-#pragma unroll
-          for (int ns = 0; ns < 8; ++ns)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) E16[(g16 * 4 + i) * 128 + ns * 16 + r16] = f32_to_bf16(acc[ms][ns][i]);
-          wave_sync_lds();
-          const int rl = lane >> 2, q = lane & 3;
-          const int rt = wm * 64 + ms * 16 + rl;
-          if (col_ok && rt < cur.rows_valid) {
-            uint16_t* dst = p.y + (size_t)(cur.row0 + rt) * p.N + col0 + q * 32;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              reinterpret_cast<uint4*>(dst)[j] = *reinterpret_cast<const uint4*>(E16 + rl * 128 + q * 32 + j * 8);
-          }
-          wave_sync_lds();
-        }
-      }
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-        for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // ---- next block ----
-    if (++kb == KB) {
-      kb = 0;
-      L += nslot;
-      if (L >= hi) break;
-      cur = decode_tile(p, offsets, smTile, NT, L);
-    }
-    next_issued = issued2;
-    st = (st + 1) % NSTAGE;
+    // stage S is free again once every wave has finished its epilogue; the
+    // next tile's first block is in stage S ^ 1 (landed at the last barrier)
+    lds_barrier();
+    if (ld.more) ld.issue(E);
+    S ^= 1;
+    if (L + nslot < hi) load_first(F, sm + S * STG, wm, wn, g16, r16);
   }
 }
 
@@ -546,7 +602,6 @@ hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const 
   s1.as = as;
   s1.a_rows = a_rows;
   s1.row_src = row_src;
-  s1.offsets = offsets;
   s1.n_groups = n_groups;
   s1.total_rows = total_rows;
   s1.K = d;
@@ -557,7 +612,7 @@ hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const 
   s1.f = f;
   s1.h = h;
   s1.hs = hs;
-  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(grid), dim3(G_THREADS), 0, stream, s1, offsets);
+  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(grid), dim3(NTHR), 0, stream, s1, offsets);
   return hipGetLastError();
 }
 
@@ -570,17 +625,16 @@ hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* of
   s2.as = hs;
   s2.a_rows = total_rows;
   s2.row_src = nullptr;
-  s2.offsets = offsets;
   s2.n_groups = n_groups;
   s2.total_rows = total_rows;
   s2.K = f;
   s2.N = d;
-  s2.n_tiles_n = (d + GNB - 1) / GNB;
+  s2.n_tiles_n = (d + BN - 1) / BN;
   s2.b = w2;
   s2.bs = w2_s;
   s2.f = f;
   s2.y = y;
-  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(grid), dim3(G_THREADS), 0, stream, s2, offsets);
+  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(grid), dim3(NTHR), 0, stream, s2, offsets);
   return hipGetLastError();
 }
 
