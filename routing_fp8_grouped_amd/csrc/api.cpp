@@ -192,6 +192,11 @@ moe_status check_gemm_shape(int n_groups, int total_rows, int d, int f) {
                 (unsigned long long)2 * f * d);
   if ((uint64_t)total_rows * (uint64_t)(d > f ? d : f) > 0xFFFFFFFFull)
     return fail(MOE_ERR_UNSUPPORTED, "total_rows*max(d,f) exceeds 4 GiB");
+  // tile list of the GEMM kernels: (m-tiles of 256 rows) x (n-tiles of 256
+  // weight rows), indexed with 32-bit integers scaled by 8
+  const uint64_t tiles = ((uint64_t)total_rows / 256 + (uint64_t)n_groups) *
+                         (uint64_t)((d > f ? d : f) / 128);
+  if (tiles >= (1ull << 28)) return fail(MOE_ERR_UNSUPPORTED, "too many GEMM tiles");
   return MOE_OK;
 }
 

@@ -138,8 +138,8 @@ struct Tile {
 // Tile l of the list: groups in order; inside a group, super-blocks of
 // SUPER_M m-tiles; inside a super-block n-tiles, and m-tiles fastest.
 __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* __restrict__ offsets,
-                                            const int* smTile, int NT, long l) {
-  const int q = (int)(l / NT);
+                                            const int* smTile, int NT, int l) {
+  const int q = l / NT;
   int a = 0, b = p.n_groups - 1;
   while (a < b) {
     const int mid = (a + b + 1) >> 1;
@@ -147,7 +147,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* __
   }
   a = __builtin_amdgcn_readfirstlane(a);   // uniform: offsets come through scalar loads
   const int mt = __builtin_amdgcn_readfirstlane(smTile[a + 1] - smTile[a]);
-  const int local = (int)(l - (long)smTile[a] * NT);
+  const int local = l - smTile[a] * NT;
   const int sb = local / (SUPER_M * NT);
   const int rem = local - sb * SUPER_M * NT;
   const int msb = min(SUPER_M, mt - sb * SUPER_M);
@@ -250,7 +250,24 @@ __device__ __forceinline__ v8i frag(const unsigned char* T, int r, int g16) {
 }
 
 // SiLU(g) * u in FP32.
-__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// SiLU(g) * u in FP32: exp(-g) to within an ulp, the quotient by the hardware
+// reciprocal (1 ulp); a few ulp from the exactly rounded value.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * u;
+}
+
+// x / s for many x with one s: the reciprocal r (hardware estimate refined by
+// one Newton step), then per x the product, its exact remainder by FMA and one
+// correction (Markstein's sequence): the correctly rounded quotient but in rare
+// cases next to a rounding boundary, where it is one ulp off.
+__device__ __forceinline__ float recip(float s) {
+  const float r = __builtin_amdgcn_rcpf(s);
+  return fmaf(fmaf(-s, r, 1.0f), r, r);
+}
+__device__ __forceinline__ float div_by(float x, float s, float r) {
+  const float q = x * r;
+  return fmaf(fmaf(-s, q, x), r, q);
+}
 
 // ---- epilogues: one 64 x 128 block per wave, written through the wave's own
 // part of the finished ring stage E, 32 rows per round ----
@@ -316,10 +333,11 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& p, const Tile& c
       for (int e = 0; e < 4; ++e) {
         const int rt = wm * 64 + (2 * r + msl) * 16 + g16 * 4 + e;
         const float sc = scale_from_amax(fmaxf(smAmax[0][rt], smAmax[1][rt]));
+        const float rs = recip(sc);
         if (WN == 0 && r16 == 0 && rt < cur.rows_valid) p.hs[(size_t)(cur.row0 + rt) * nhs + cur.n] = sc;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t q = f32x2_to_e4m3(acc[2 * r + msl][KEEP + j][e] / sc, 0.0f) & 0xFFu;
+          const uint32_t q = f32x2_to_e4m3(div_by(acc[2 * r + msl][KEEP + j][e], sc, rs), 0.0f) & 0xFFu;
           Q[(msl * 16 + g16 * 4 + e) * 64 + j * 16 + r16] = (unsigned char)q;
         }
       }
@@ -382,8 +400,8 @@ struct Loader {
   const int* smTile;
   int (*smRows)[BM];
   int NT, KB, wave, lane, nslot;
-  long hi;
-  long L;
+  int hi;
+  int L;
   int kb, par;
   bool more;
   uint32_t* srcw;          // this wave's source table in LDS
@@ -525,11 +543,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_kernel(GemmArgs p,
     if (lane == 0) smTile[0] = 0;
   }
   __syncthreads();
-  const long total = (long)smTile[p.n_groups] * NT;
+  // the host guarantees fewer than 2^31 / 8 tiles
+  const int total = smTile[p.n_groups] * NT;
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int nslot = gridDim.x >> 3;
-  const long lo = total * xcd / 8, hi = total * (xcd + 1) / 8;
+  const int lo = total * xcd / 8, hi = total * (xcd + 1) / 8;
   if (lo + slot >= hi) return;
 
   Loader<SWIGLU> ld{p, offsets, smTile, smRows, NT, KB, wave, lane, nslot, hi, lo + slot, 0, 0, true,
@@ -547,7 +566,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_kernel(GemmArgs p,
   Frags F;
   load_first(F, sm, wm, wn, g16, r16);
   int S = 0;   // ring stage of the block being multiplied
-  for (long L = lo + slot; L < hi; L += nslot) {
+  for (int L = lo + slot; L < hi; L += nslot) {
     const Tile cur = decode_tile(p, offsets, smTile, NT, L);
     v4f acc[4][8];
 #pragma unroll

@@ -162,7 +162,9 @@ def h_code_ambiguity(aq_rows, as_rows, w13q, w13s, g, u, h, hs):
     eg, eu = e[:, :f], e[:, f:]
     sig = 1.0 / (1.0 + np.exp(-g))
     dsilu = sig * (1.0 + g * (1.0 - sig))
-    eh = np.abs(u) * np.abs(dsilu) * eg + np.abs(g * sig) * eu + 2.0 ** -22 * np.abs(h)
+    # FP32 SwiGLU: the kernel's SiLU (exp within an ulp, hardware reciprocal)
+    # and the product with u sit a few ulp from the exactly rounded value
+    eh = np.abs(u) * np.abs(dsilu) * eg + np.abs(g * sig) * eu + 2.0 ** -20 * np.abs(h)
     rows = h.shape[0]
     ht = np.abs(h).reshape(rows, -1, 128)
     et = eh.reshape(rows, -1, 128)
