@@ -461,10 +461,18 @@ __device__ __forceinline__ void load_first(Frags& F, const unsigned char* stage,
 // `cur` (column 7's fragment) comes the ring barrier; unless LAST, the stage
 // is then refilled (the loader's next block) and the first fragments of the
 // next block are read from `nxt` while column 7 is multiplied.
+//
+// A wave whose 64 rows all lie past the end of a partial tile (`active` false)
+// skips the reads and the arithmetic but keeps the barrier and the loads.
 template <bool SWIGLU, bool LAST>
 __device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGLU>& ld,
                                         unsigned char* cur, const unsigned char* nxt, int wm, int wn,
-                                        int g16, int r16) {
+                                        int g16, int r16, bool active) {
+  if (!active) {
+    ring_barrier();
+    if (!LAST && ld.more) ld.issue(cur);
+    return;
+  }
   const unsigned char* Bc = cur + ST_A;
   v4f part[2];
 #pragma unroll
@@ -564,7 +572,6 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_kernel(GemmArgs p,
   if (ld.more) ld.issue(sm + STG);
 
   Frags F;
-  load_first(F, sm, wm, wn, g16, r16);
   int S = 0;   // ring stage of the block being multiplied
   for (int L = lo + slot; L < hi; L += nslot) {
     const Tile cur = decode_tile(p, offsets, smTile, NT, L);
@@ -573,11 +580,14 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_kernel(GemmArgs p,
     for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
       for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = v4f{0.f, 0.f, 0.f, 0.f};
+    // rows wm*64 .. +63 hold data (uniform per wave)
+    const bool active = wm * 64 < cur.rows_valid;
+    if (active) load_first(F, sm + S * STG, wm, wn, g16, r16);
     for (int kb = 0; kb < KB - 1; ++kb) {
-      k_block<SWIGLU, false>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16);
+      k_block<SWIGLU, false>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16, active);
       S ^= 1;
     }
-    k_block<SWIGLU, true>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16);
+    k_block<SWIGLU, true>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16, active);
 
     // ---- epilogue, through stage S (every wave has finished reading it: the
     // ring barrier of the last block followed the last read) ----
@@ -593,7 +603,6 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_kernel(GemmArgs p,
     lds_barrier();
     if (ld.more) ld.issue(E);
     S ^= 1;
-    if (L + nslot < hi) load_first(F, sm + S * STG, wm, wn, g16, r16);
   }
 }
 
