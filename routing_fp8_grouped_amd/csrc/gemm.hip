@@ -69,7 +69,7 @@ struct GemmArgs {
 // r0..r0+15 at one chunk; swz gives rows r0..r0+7 eight different positions
 // and gives the even rows and the odd rows of r0..r0+15 eight positions each,
 // so the read is conflict-free whether 8 or 16 lanes are served per cycle.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+__device__ __forceinline__ int swz(int r) { return op_swz(r); }
 __device__ __forceinline__ int op_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 4); }
 
 // ---- LDS ring: two K blocks, filled by direct global->LDS loads ----
@@ -85,45 +85,6 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Direct global->LDS loads.  Lane l of the wave writes its 16 (or 4) bytes at
-// LDS byte address lds + 16 l (4 l); the source address is per lane.  They are
-// issued from inline assembly so that the compiler does not track them: it
-// would otherwise make every later LDS read wait for all of them, which would
-// drain the pipeline each K block.  The instructions have no register outputs
-// (the data goes to LDS); every LDS read of their data follows an explicit
-// vmcnt wait and a barrier, and every reuse of a ring slot follows a barrier.
-// M0 carries the LDS address; the compiler does not allocate it.
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
-}
-// base: wave-uniform global address; off: per-lane byte offset (32 bits).
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory");
-}
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(off), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Wait for all of this wave's LDS reads and direct loads, then barrier.  The
-// barrier is written in assembly with a memory clobber so that the compiler
-// moves no LDS access across it.
-__device__ __forceinline__ void ring_barrier() {
-  // gfx9 s_waitcnt fields: vmcnt[3:0] bits 3:0, expcnt 6:4, lgkmcnt 11:8,
-  // vmcnt[5:4] bits 15:14
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0), expcnt unconstrained
-  asm volatile("s_barrier" ::: "memory");
-}
 // Barrier for LDS data only: waits for this wave's LDS operations, not for the
 // direct loads in flight.
 __device__ __forceinline__ void lds_barrier() {

@@ -4,11 +4,13 @@
 // "The router's affinity scores", "Selecting and combining experts", and
 // chapter 8 "V3's routing-only bias", "Restricting target nodes").
 //
-// One workgroup routes 64 tokens against all (<= 256) experts:
-//   1. logits: BF16 MFMA 16x16x32 with FP32 accumulation over each 128-wide K
-//      chunk, chunks summed in FP64 registers.  The token tile is staged in
-//      LDS; each wave streams the centroid rows of its 64 experts straight from
-//      global memory (they are shared by every workgroup and stay in L2/MALL).
+// One workgroup (8 waves) routes 64 tokens against all (<= 256) experts:
+//   1. logits: BF16 MFMA 16x16x32, FP32 partial sums over each 128-wide chunk
+//      of d, chunks summed in FP64 registers.  Token rows and centroid rows
+//      stream through a two-stage LDS ring (64 elements of d per stage) by
+//      direct global->LDS loads; wave w owns experts 32 w .. 32 w + 31.  The
+//      FP64 logits are stored to LDS rounded to FP32 (relative 6e-8: the
+//      biased scores move by < 1e-7, far inside the 1e-6 near-tie band).
 //   2. selection, one token per wave at a time, in FP64: per-group sum of the
 //      k/M largest biased scores, top-M groups and top-k experts by wavefront
 //      argmax reductions (ties to the lower index), gates from the unbiased
@@ -22,7 +24,14 @@ namespace moe {
 
 constexpr int RT_TOK = 64;
 constexpr int RT_EXP = 256;
-constexpr int RT_KC = 128;
+constexpr int RT_THREADS = 512;
+constexpr int RT_KS = 32;                              // d elements per ring stage
+constexpr int RT_ROWB = RT_KS * 2;                     // 64-byte rows
+constexpr int RT_A = RT_TOK * RT_ROWB;                 // token rows of a stage, 4 KB
+constexpr int RT_STG = (RT_TOK + RT_EXP) * RT_ROWB;    // 20 KB
+constexpr int RT_NST = 6;                              // ring depth
+constexpr int RT_LSTRIDE = RT_EXP + 1;                 // FP32 logit table row stride
+constexpr int RT_MAXG = 64;
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -30,236 +39,270 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Wavefront argmax over (value, index): larger value wins, equal values go to
-// the smaller index.  Every lane returns the same pair.
-__device__ __forceinline__ void wave_argmax(double& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double ov = __shfl_xor(v, o);
-    const int oi = __shfl_xor(i, o);
-    if (ov > v || (ov == v && oi < i)) {
-      v = ov;
-      i = oi;
-    }
-  }
+// LDS layout of a 64-byte row r: its 16-byte chunk c sits at c ^ ((r >> 2) & 3),
+// so a fragment read (16 lanes on rows r0..r0+15, one chunk) covers all banks.
+__device__ __forceinline__ int rt_off(int r, int c) { return r * RT_ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
+
+__device__ __forceinline__ v8bf rt_frag(const unsigned char* T, int r, int c) {
+  return *reinterpret_cast<const v8bf*>(T + rt_off(r, c));
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// s_waitcnt vmcnt(N) only (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void rt_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | (((N >> 4) & 3) << 14));
 }
 
-__device__ __forceinline__ int a_lds_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+__device__ __forceinline__ float sigmoid32(float l) {
+  return __builtin_amdgcn_rcpf(1.0f + expf(-l));
+}
 
-__global__ __launch_bounds__(256) void route_kernel(const uint16_t* __restrict__ x,
-                                                    const uint16_t* __restrict__ wg,
-                                                    const float* __restrict__ bias, int T, int d,
-                                                    int E, int G, int M, int k, double route_scale,
-                                                    int32_t* __restrict__ idx,
-                                                    float* __restrict__ wout) {
-  __shared__ __attribute__((aligned(16))) unsigned char a_lds[RT_TOK * RT_KC * 2];
-  __shared__ double logit[RT_TOK][RT_EXP + 1];
-  __shared__ double zbuf[4][RT_EXP];
+__global__ __launch_bounds__(RT_THREADS) void route_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wg,
+                                                           const float* __restrict__ bias, int T,
+                                                           int d, int E, int G, int M, int k,
+                                                           double route_scale,
+                                                           int32_t* __restrict__ idx,
+                                                           float* __restrict__ wout) {
+  // ring of RT_NST stages; after the logits it holds the FP32 logit table
+  __shared__ __attribute__((aligned(16))) unsigned char ring[RT_NST * RT_STG];
+  __shared__ float gscore[RT_MAXG][RT_TOK];
+  __shared__ float sbias[RT_EXP];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g16 = lane >> 4, r16 = lane & 15;
   const int t0 = blockIdx.x * RT_TOK;
-  const int n_kc = d / RT_KC;
+  const int n_ks = d / RT_KS;
+  if (threadIdx.x < RT_EXP) sbias[threadIdx.x] = (bias && (int)threadIdx.x < E) ? bias[threadIdx.x] : 0.0f;
 
-  // Token-tile loads: thread owns 4 16-byte chunks of the 64 x 256-byte tile.
-  const uint16_t* a_src[4];
-  int a_dst[4];
-  bool a_ok[4];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int id = threadIdx.x + 256 * it;
-    const int r = id >> 4, c = id & 15;
-    a_ok[it] = (t0 + r) < T;
-    a_src[it] = x + (size_t)(a_ok[it] ? t0 + r : 0) * d + c * 8;
-    a_dst[it] = a_lds_off(r, c);
+  // ---- logits ----
+  // Direct loads: an instruction writes 1 KB = 16 rows of 64 bytes; lane l
+  // fills row 16 i + l / 4, physical chunk l % 4 with the logical chunk
+  // (l % 4) ^ ((row >> 2) & 3).  Wave w loads expert rows 32 w .. 32 w + 31 (its
+  // own experts) and, for w < 4, token rows 16 w .. 16 w + 15; rows past T or E
+  // repeat the last valid row (their results are never used).
+  const int pc = lane & 3;
+  uint32_t a_off = 0, b_off[2];
+  if (wave < 4) {
+    const int r = wave * 16 + (lane >> 2);
+    const int t = min(t0 + r, T - 1);
+    a_off = (uint32_t)t * (uint32_t)d * 2u + (uint32_t)((pc ^ ((r >> 2) & 3)) * 16);
   }
-  // Centroid rows of this wave's experts: lane reads 32 BF16 of row e per chunk.
-  const uint16_t* b_src[4];
-  bool b_ok[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int e = 64 * wave + 16 * nt + r16;
-    b_ok[nt] = e < E;
-    b_src[nt] = wg + (size_t)(b_ok[nt] ? e : 0) * d + g16 * 32;
+  for (int i = 0; i < 2; ++i) {
+    const int r = wave * 32 + i * 16 + (lane >> 2);
+    const int e = min(r, E - 1);
+    b_off[i] = (uint32_t)e * (uint32_t)d * 2u + (uint32_t)((pc ^ ((r >> 2) & 3)) * 16);
   }
+  const uint32_t ring0 = lds_addr(ring);
+#define RT_ISSUE(ks_)                                                                        \
+  do {                                                                                       \
+    const int ks__ = (ks_);                                                                  \
+    const uint32_t base__ = ring0 + (ks__ % RT_NST) * RT_STG;                                \
+    if (wave < 4) dma16(x + (size_t)ks__ * RT_KS, a_off, base__ + wave * 1024);              \
+    dma16(wg + (size_t)ks__ * RT_KS, b_off[0], base__ + RT_A + (wave * 2) * 1024);           \
+    dma16(wg + (size_t)ks__ * RT_KS, b_off[1], base__ + RT_A + (wave * 2 + 1) * 1024);       \
+  } while (0)
 
-  double acc64[4][4][4];
+  double acc64[4][2][4];
+  v4f acc[4][2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 2; ++nt) {
+      acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc64[mt][nt][i] = 0.0;
-
-  uint4 a_next[4];
-  uint4 b_next[4][4];
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int it = 0; it < 4; ++it)
-    a_next[it] = a_ok[it] ? *reinterpret_cast<const uint4*>(a_src[it]) : zero4;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      b_next[nt][q] = b_ok[nt] ? *reinterpret_cast<const uint4*>(b_src[nt] + q * 8) : zero4;
-
-  for (int kc = 0; kc < n_kc; ++kc) {
-    __syncthreads();  // every wave is done reading the previous token tile
-#pragma unroll
-    for (int it = 0; it < 4; ++it) *reinterpret_cast<uint4*>(a_lds + a_dst[it]) = a_next[it];
-    uint4 b_cur[4][4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) b_cur[nt][q] = b_next[nt][q];
-    __syncthreads();
-    if (kc + 1 < n_kc) {
-      const size_t off = (size_t)(kc + 1) * RT_KC;
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-        a_next[it] = a_ok[it] ? *reinterpret_cast<const uint4*>(a_src[it] + off) : zero4;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          b_next[nt][q] = b_ok[nt] ? *reinterpret_cast<const uint4*>(b_src[nt] + off + q * 8) : zero4;
     }
-    v4f acc[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      v8bf af[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int r = mt * 16 + r16;
-        af[mt] = *reinterpret_cast<const v8bf*>(a_lds + a_lds_off(r, g16 * 4 + kk));
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const v8bf bf = __builtin_bit_cast(v8bf, b_cur[nt][kk]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_bf16_16x16x32(af[mt], bf, acc[mt][nt]);
-      }
+
+  // stages 0 .. RT_NST-2 in flight (d >= 128, so n_ks >= 4)
+  for (int ks = 0; ks < RT_NST - 1 && ks < n_ks; ++ks) RT_ISSUE(ks);
+  for (int ks = 0; ks < n_ks; ++ks) {
+    // stage ks has landed once at most the younger stages are outstanding
+    const int younger = min(RT_NST - 2, n_ks - 1 - ks);
+    if (younger >= RT_NST - 2) {
+      if (wave < 4) rt_wait_vmcnt<3 * (RT_NST - 2)>(); else rt_wait_vmcnt<2 * (RT_NST - 2)>();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the tail of the loop
     }
+    asm volatile("s_barrier" ::: "memory");   // all waves' loads visible; stage ks-1 free
+    if (ks + RT_NST - 1 < n_ks) RT_ISSUE(ks + RT_NST - 1);
+    const unsigned char* A = ring + (ks % RT_NST) * RT_STG;
+    const unsigned char* B = A + RT_A;
+    v8bf af[4], bf[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) af[mt] = rt_frag(A, mt * 16 + r16, g16);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 2; ++nt) bf[nt] = rt_frag(B, wave * 32 + nt * 16 + r16, g16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc64[mt][nt][i] += (double)acc[mt][nt][i];
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_bf16_16x16x32(af[mt], bf[nt], acc[mt][nt]);
+    if ((ks & 3) == 3) {   // a 128-wide chunk of d is complete: promote to FP64
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc64[mt][nt][i] += (double)acc[mt][nt][i];
+          acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    }
   }
+#undef RT_ISSUE
+  __syncthreads();   // every wave is done with the ring
 
+  // FP32 logit table [token][expert] over the ring
+  float* logit = reinterpret_cast<float*>(ring);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        logit[mt * 16 + g16 * 4 + i][64 * wave + 16 * nt + r16] = acc64[mt][nt][i];
+        logit[(mt * 16 + g16 * 4 + i) * RT_LSTRIDE + wave * 32 + nt * 16 + r16] = (float)acc64[mt][nt][i];
   __syncthreads();
 
-  // ---- selection: wave `wave` routes tokens wave, wave+4, ... of the tile ----
+  // ---- selection: a team of 8 lanes per token (wave w, lanes 8 j .. 8 j + 7
+  // route token 8 w + j); member m handles the groups g = m mod 8 ----
+  // Biased scores z = sigmoid(l) + b in FP32 (within ~1e-7 of the exact
+  // value, far inside the 1e-6 near-tie band); the gates use the FP64
+  // affinity of the selected experts.
+  const int tt = wave * 8 + (lane >> 3);
+  const int mem = lane & 7;
+  const int t = t0 + tt;
+  const float* L = logit + tt * RT_LSTRIDE;
   const int per = E / G;
   const int n_top = k / M;
-  const double NEG_INF = -__builtin_huge_val();
-  for (int tt = wave; tt < RT_TOK; tt += 4) {
-    const int t = t0 + tt;
-    if (t >= T) break;
-    double zc[4];
+  const float NEG = -__builtin_huge_valf();
+  // 1. group scores: sum of the n_top largest biased scores of each group
+  for (int g = mem; g < G; g += 8) {
+    float top[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      zc[j] = NEG_INF;
-      if (e < E) {
-        const double s = 1.0 / (1.0 + exp(-logit[tt][e]));
-        const double z = s + (bias ? (double)bias[e] : 0.0);
-        zbuf[wave][e] = z;
-        zc[j] = z;
-      }
-    }
-    wave_sync_lds();
-    // group scores: lane g sums the n_top largest biased scores of group g
-    double gv = NEG_INF;
-    if (lane < G) {
-      double top[8];
+    for (int i = 0; i < 8; ++i) top[i] = NEG;
+    for (int e = g * per; e < (g + 1) * per; ++e) {
+      float v = sigmoid32(L[e]) + sbias[e];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) top[i] = NEG_INF;
-      for (int e = lane * per; e < (lane + 1) * per; ++e) {
-        double v = zbuf[wave][e];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (i < n_top && v > top[i]) {
-            const double tmp = top[i];
-            top[i] = v;
-            v = tmp;
-          }
+      for (int i = 0; i < 8; ++i) {
+        if (i < n_top && v > top[i]) {
+          const float tmp = top[i];
+          top[i] = v;
+          v = tmp;
         }
       }
-      gv = 0.0;
+    }
+    float gs = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < n_top) gv += top[i];
+    for (int i = 0; i < 8; ++i)
+      if (i < n_top) gs += top[i];
+    gscore[g][tt] = gs;
+  }
+  wave_sync_lds();
+  // 2. the M best groups (ties to the lower group index), on every member
+  uint64_t gmask = 0;
+  for (int r = 0; r < M; ++r) {
+    float bv = NEG;
+    int bg = -1;
+    for (int g = 0; g < G; ++g) {
+      const float v = gscore[g][tt];
+      if (!((gmask >> g) & 1ull) && (bg < 0 || v > bv)) {
+        bv = v;
+        bg = g;
+      }
     }
-    wave_sync_lds();  // zbuf is rewritten by the next token
-    uint64_t gmask = 0;
-    for (int r = 0; r < M; ++r) {
-      double v = gv;
-      int i = lane;
-      wave_argmax(v, i);
-      gmask |= 1ull << i;
-      if (lane == i) gv = NEG_INF;
-    }
+    gmask |= 1ull << bg;
+  }
+  // 3. each member: the k best experts of its kept groups, best first (ties
+  // to the lower id: experts are visited in ascending order and only a
+  // strictly larger score moves an entry down)
+  float sv[16];
+  int si[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !((gmask >> (e / per)) & 1ull)) zc[j] = NEG_INF;
+  for (int i = 0; i < 16; ++i) {
+    sv[i] = NEG;
+    si[i] = 0x7fffffff;
+  }
+  for (int g = mem; g < G; g += 8) {
+    if (!((gmask >> g) & 1ull)) continue;
+    for (int e = g * per; e < (g + 1) * per; ++e) {
+      float v = sigmoid32(L[e]) + sbias[e];
+      int vi = e;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < k && (si[i] == 0x7fffffff || v > sv[i])) {
+          const float tv = sv[i];
+          const int ti = si[i];
+          sv[i] = v;
+          si[i] = vi;
+          v = tv;
+          vi = ti;
+        }
+      }
     }
-    int sel[16];
-    bool taken[4] = {false, false, false, false};
+  }
+  // 4. merge the 8 sorted lists: k rounds of a team argmax over the heads
+  // (larger score, then lower id); the winner's list moves up by one
+  int sel[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sel[r] = 0x7fffffff;
+    if (r < k) {
+      float bv = sv[0];
+      int bi = si[0];
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        const bool take = (oi != 0x7fffffff) && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
+        if (take) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      sel[r] = bi;
+      if (si[0] == bi) {
+#pragma unroll
+        for (int i = 0; i < 15; ++i) {
+          sv[i] = sv[i + 1];
+          si[i] = si[i + 1];
+        }
+        sv[15] = NEG;
+        si[15] = 0x7fffffff;
+      }
+    }
+  }
+  // 5. ascending ids with their gates w = route_scale * s / sum(s) in FP64;
+  // member m computes the entries r = m, m + 8
+  double s_part = 0.0;
+  double s_mine[2] = {0.0, 0.0};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sel[r] = 0x7fffffff;
-      if (r < k) {
-        double bv = NEG_INF;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = lane + 64 * j;
-          if (e < E && !taken[j] && zc[j] != NEG_INF && (zc[j] > bv || (zc[j] == bv && e < be))) {
-            bv = zc[j];
-            be = e;
-          }
-        }
-        wave_argmax(bv, be);
-        sel[r] = be;
-        if (be < E && (be & 63) == lane) taken[be >> 6] = true;
+      if (r == mem + 8 * h && r < k) {
+        s_mine[h] = 1.0 / (1.0 + exp(-(double)L[sel[r]]));
+        s_part += s_mine[h];
       }
     }
-    // lane j < k: expert sel[j], its rank among the selected ids, its gate
-    int my_e = 0x7fffffff;
+  }
+  double ssum = s_part;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (r == lane) my_e = sel[r];
-    int rank = 0;
+  for (int o = 1; o < 8; o <<= 1) ssum += __shfl_xor(ssum, o);
+  if (t < T) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (r < k && sel[r] < my_e) ++rank;
-    double s = 0.0;
-    const bool mine = lane < k && my_e < E;
-    if (mine) s = 1.0 / (1.0 + exp(-logit[tt][my_e]));
-    const double ssum = wave_sum(s);
-    if (mine) {
-      idx[(size_t)t * k + rank] = my_e;
-      wout[(size_t)t * k + rank] = (float)(route_scale * s / ssum);
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (r == mem + 8 * h && r < k) {
+          int rank = 0;
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (j < k && sel[j] < sel[r]) ++rank;
+          idx[(size_t)t * k + rank] = sel[r];
+          wout[(size_t)t * k + rank] = (float)(route_scale * s_mine[h] / ssum);
+        }
+      }
     }
   }
 }
@@ -268,7 +311,7 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wg, const float* bias
                         int E, int G, int M, int k, float route_scale, int32_t* idx, float* w,
                         hipStream_t stream) {
   const int blocks = (T + RT_TOK - 1) / RT_TOK;
-  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(256), 0, stream, x, wg, bias, T, d, E, G, M,
+  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(RT_THREADS), 0, stream, x, wg, bias, T, d, E, G, M,
                      k, (double)route_scale, idx, w);
   return hipGetLastError();
 }
