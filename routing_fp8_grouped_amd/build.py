@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["api.cpp", "quant.hip", "route.hip", "permute.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["api.cpp", "quant.hip", "route.hip", "permute.hip", "gemm.hip", "gemm_small.hip",
+           "combine.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 

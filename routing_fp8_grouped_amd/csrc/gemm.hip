@@ -585,6 +585,9 @@ hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const 
                           const int32_t* offsets, int n_groups, int total_rows, int d, int f,
                           const uint8_t* w13, const float* w13_s, uint8_t* h, float* hs,
                           hipStream_t stream) {
+  if (total_rows <= 16 * n_groups)   // few rows per group: stream the weights
+    return launch_gemm_up_small(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d, f, w13,
+                                w13_s, h, hs, stream);
   const int grid = ((num_cus() + 7) / 8) * 8;
   GemmArgs s1{};
   s1.a = aq;
@@ -608,6 +611,8 @@ hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const 
 hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* offsets, int n_groups,
                             int total_rows, int d, int f, const uint8_t* w2, const float* w2_s,
                             uint16_t* y, hipStream_t stream) {
+  if (total_rows <= 16 * n_groups)
+    return launch_gemm_down_small(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y, stream);
   const int grid = ((num_cus() + 7) / 8) * 8;
   GemmArgs s2{};
   s2.a = h;

@@ -1,0 +1,279 @@
+// Grouped FP8 GEMM of the SwiGLU experts for few rows per expert (decode-sized
+// batches): the same computation as grouped_gemm_kernel (the "DeepSeek-V3"
+// summary page, section 6; the book's chapter 16 "Periodic high-precision
+// promotion", chapter 17), organised for streaming the expert weights from HBM
+// rather than for reuse.
+//
+// A tile is at most 16 rows of one group (an "m-chunk") against 256 weight
+// rows.  Each of the 8 waves owns 32 weight rows and streams their FP8 codes
+// from global memory straight into registers, SM_D K blocks ahead, with no
+// LDS ring and no barrier inside the K loop; it reads the tile's 16 activation
+// rows the same way (they are shared by the waves and stay in L2).  In stage 1
+// wave w owns the gate rows w*16 .. +15 and the matching up rows, so SiLU(g)*u
+// is formed in registers; the 1x128 amax across the 8 waves goes through LDS.
+// Scales: the rows' activation scales and the two weight-scale columns of the
+// tile are staged in LDS once per tile.  Promotion as in the large kernel: one
+// 16x16x128 MFMA per K block and output block, its partial sum multiplied by
+// activation scale x weight scale and added to an FP32 accumulator.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int SM_M = 16;          // rows per m-chunk
+constexpr int SM_THREADS = 512;   // 8 waves
+constexpr int SM_D = 6;           // K blocks of loads in flight per wave
+constexpr int SM_MAX_KB = 128;    // K <= 16384
+constexpr int SM_MAX_GROUPS = 1024;
+
+struct SmallArgs {
+  const uint8_t* a;         // [a_rows, K] E4M3
+  const float* as;          // [a_rows, K/128]
+  int a_rows;
+  const int32_t* row_src;   // [total rows] or null (identity)
+  int n_groups;
+  int total_rows;
+  int K;
+  int N;                    // weight rows per group
+  int n_tiles_n;            // 256-row weight blocks per group
+  const uint8_t* b;         // [n_groups, N, K]
+  const float* bs;          // [n_groups, N/128, K/128]
+  int f;                    // stage 1: N = 2f
+  uint8_t* h;
+  float* hs;
+  uint16_t* y;
+};
+
+struct Frag3 {
+  v8i a, b0, b1;
+};
+
+__device__ __forceinline__ v8i load_frag(const uint8_t* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
+    SmallArgs p, const int32_t* __restrict__ offsets) {
+  __shared__ int smTile[SM_MAX_GROUPS + 1];        // m-chunk prefix over groups
+  __shared__ __attribute__((aligned(16))) float sSA[SM_MAX_KB][SM_M];   // [kb][row]
+  __shared__ float sSW[2][SM_MAX_KB];              // weight scales of column sets 0 / 1
+  __shared__ float sAmax[SM_THREADS / 64][SM_M];
+  __shared__ int sRow[SM_M];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int KB = p.K / 128;
+  const int NT = p.n_tiles_n;
+
+  if (wave == 0) {
+    int carry = 0;
+    for (int base = 0; base < p.n_groups; base += 64) {
+      const int g = base + lane;
+      int mt = 0;
+      if (g < p.n_groups) mt = (offsets[g + 1] - offsets[g] + SM_M - 1) / SM_M;
+      int v = mt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+      }
+      if (g < p.n_groups) smTile[g + 1] = carry + v;
+      carry += __shfl(v, 63);
+    }
+    if (lane == 0) smTile[0] = 0;
+  }
+  __syncthreads();
+  // the host guarantees fewer than 2^31 / 8 tiles
+  const int total = smTile[p.n_groups] * NT;
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int nslot = gridDim.x >> 3;
+  const int lo = total * xcd / 8, hi = total * (xcd + 1) / 8;
+
+  for (int l = lo + slot; l < hi; l += nslot) {
+    // tile l: group by binary search over the m-chunk prefix, then n-major,
+    // m-chunk fastest (the chunks sharing a weight block run together)
+    const int q = l / NT;
+    int ga = 0, gb = p.n_groups - 1;
+    while (ga < gb) {
+      const int mid = (ga + gb + 1) >> 1;
+      if (smTile[mid] <= q) ga = mid; else gb = mid - 1;
+    }
+    const int g = __builtin_amdgcn_readfirstlane(ga);
+    const int mt = __builtin_amdgcn_readfirstlane(smTile[g + 1] - smTile[g]);
+    const int local = l - smTile[g] * NT;
+    const int n = local / mt;
+    const int m = local - n * mt;
+    const int row0 = offsets[g] + m * SM_M;
+    const int rows_valid = min(SM_M, min(offsets[g + 1], p.total_rows) - row0);
+
+    // ---- stage the rows' sources and scales ----
+    if (tid < SM_M) {
+      const int rr = min(max(row0 + min(tid, rows_valid - 1), 0), p.total_rows - 1);
+      int src = p.row_src ? p.row_src[rr] : rr;
+      sRow[tid] = min(max(src, 0), p.a_rows - 1);
+    }
+    __syncthreads();
+    for (int i = tid; i < KB * SM_M; i += SM_THREADS) {
+      const int r = i / KB, kb = i - r * KB;
+      sSA[kb][r] = p.as[(size_t)sRow[r] * KB + kb];
+    }
+    const int nsb = p.N / 128;
+    for (int i = tid; i < 2 * KB; i += SM_THREADS) {
+      const int c = i / KB, kb = i - c * KB;
+      int sb;
+      if (SWIGLU) sb = c ? p.f / 128 + n : n;
+      else sb = min(2 * n + c, nsb - 1);
+      sSW[c][kb] = p.bs[(size_t)(g * nsb + sb) * KB + kb];
+    }
+    __syncthreads();
+
+    // ---- this wave's operands: activation row sRow[r16]; weight rows of the
+    // two 16-column blocks (stage 1: gate and up of h columns wave*16 .. +15;
+    // stage 2: rows wave*32 .. +31 of the 256-row block) ----
+    const uint8_t* pa = p.a + (size_t)sRow[r16] * p.K + g16 * 32;
+    int wr0, wr1;
+    if (SWIGLU) {
+      wr0 = n * 128 + wave * 16 + r16;
+      wr1 = p.f + n * 128 + wave * 16 + r16;
+    } else {
+      wr0 = n * 256 + wave * 32 + r16;
+      wr1 = wr0 + 16;
+    }
+    const bool col0_ok = SWIGLU || wr0 - r16 < p.N;
+    const bool col1_ok = SWIGLU || wr1 - r16 < p.N;
+    wr0 = min(wr0, p.N - 1);
+    wr1 = min(wr1, p.N - 1);
+    const uint8_t* gb_ = p.b + (size_t)g * p.N * p.K;
+    const uint8_t* pb0 = gb_ + (size_t)wr0 * p.K + g16 * 32;
+    const uint8_t* pb1 = gb_ + (size_t)wr1 * p.K + g16 * 32;
+    // stage 2: waves 0..3 lie in weight-scale block 2n, waves 4..7 in 2n+1
+    const int swc0 = SWIGLU ? 0 : (wave >= 4 ? 1 : 0);
+    const int swc1 = SWIGLU ? 1 : swc0;
+
+    v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
+    Frag3 buf[SM_D];
+#pragma unroll
+    for (int j = 0; j < SM_D; ++j) {
+      if (j < KB) {
+        buf[j].a = load_frag(pa + j * 128);
+        buf[j].b0 = load_frag(pb0 + j * 128);
+        buf[j].b1 = load_frag(pb1 + j * 128);
+      }
+    }
+    for (int kb0 = 0; kb0 < KB; kb0 += SM_D) {
+#pragma unroll
+      for (int j = 0; j < SM_D; ++j) {
+        const int kb = kb0 + j;
+        if (kb < KB) {
+          const v4f p0 = mfma_fp8_16x16x128(buf[j].a, buf[j].b0, v4f{0.f, 0.f, 0.f, 0.f});
+          const v4f p1 = mfma_fp8_16x16x128(buf[j].a, buf[j].b1, v4f{0.f, 0.f, 0.f, 0.f});
+          if (kb + SM_D < KB) {
+            buf[j].a = load_frag(pa + (kb + SM_D) * 128);
+            buf[j].b0 = load_frag(pb0 + (kb + SM_D) * 128);
+            buf[j].b1 = load_frag(pb1 + (kb + SM_D) * 128);
+          }
+          const float4 sa = *reinterpret_cast<const float4*>(&sSA[kb][g16 * 4]);
+          const float s0 = sSW[swc0][kb], s1 = sSW[swc1][kb];
+          acc0[0] = fmaf(p0[0], sa.x * s0, acc0[0]);
+          acc0[1] = fmaf(p0[1], sa.y * s0, acc0[1]);
+          acc0[2] = fmaf(p0[2], sa.z * s0, acc0[2]);
+          acc0[3] = fmaf(p0[3], sa.w * s0, acc0[3]);
+          acc1[0] = fmaf(p1[0], sa.x * s1, acc1[0]);
+          acc1[1] = fmaf(p1[1], sa.y * s1, acc1[1]);
+          acc1[2] = fmaf(p1[2], sa.z * s1, acc1[2]);
+          acc1[3] = fmaf(p1[3], sa.w * s1, acc1[3]);
+        }
+      }
+    }
+
+    // ---- epilogue: lane holds rows g16*4 + i, column r16 of its blocks ----
+    if (SWIGLU) {
+      float hv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float gv = acc0[i], uv = acc1[i];
+        hv[i] = gv * __builtin_amdgcn_rcpf(1.0f + expf(-gv)) * uv;
+        float a = fabsf(hv[i]);
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+        if (r16 == 0) sAmax[wave][g16 * 4 + i] = a;
+      }
+      __syncthreads();
+      const int nhs = p.f / 128;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = g16 * 4 + i;
+        float a = sAmax[0][r];
+#pragma unroll
+        for (int w = 1; w < SM_THREADS / 64; ++w) a = fmaxf(a, sAmax[w][r]);
+        const float sc = scale_from_amax(a);
+        if (r < rows_valid) {
+          const float rs = __builtin_amdgcn_rcpf(sc);
+          const float r1 = fmaf(fmaf(-sc, rs, 1.0f), rs, rs);   // reciprocal, one Newton step
+          const float q0 = hv[i] * r1;
+          const float qv = fmaf(fmaf(-sc, q0, hv[i]), r1, q0);  // h / sc, one correction
+          p.h[(size_t)(row0 + r) * p.f + n * 128 + wave * 16 + r16] =
+              (uint8_t)(f32x2_to_e4m3(qv, 0.0f) & 0xFFu);
+          if (wave == 0 && r16 == 0) p.hs[(size_t)(row0 + r) * nhs + n] = sc;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = g16 * 4 + i;
+        if (r < rows_valid) {
+          uint16_t* dst = p.y + (size_t)(row0 + r) * p.N + n * 256 + wave * 32 + r16;
+          if (col0_ok) dst[0] = f32_to_bf16(acc0[i]);
+          if (col1_ok) dst[16] = f32_to_bf16(acc1[i]);
+        }
+      }
+    }
+    __syncthreads();   // sRow, sSA, sSW, sAmax are rewritten by the next tile
+  }
+}
+
+static int g_num_cus_small[64];
+
+static int num_cus_small() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (g_num_cus_small[dev] == 0) {
+    int nc = 0;
+    if (hipDeviceGetAttribute(&nc, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || nc <= 0)
+      nc = 256;
+    g_num_cus_small[dev] = nc;
+  }
+  return g_num_cus_small[dev];
+}
+
+hipError_t launch_gemm_up_small(const uint8_t* aq, const float* as, int a_rows,
+                                const int32_t* row_src, const int32_t* offsets, int n_groups,
+                                int total_rows, int d, int f, const uint8_t* w13,
+                                const float* w13_s, uint8_t* h, float* hs, hipStream_t stream) {
+  SmallArgs s{};
+  s.a = aq; s.as = as; s.a_rows = a_rows; s.row_src = row_src; s.n_groups = n_groups;
+  s.total_rows = total_rows; s.K = d; s.N = 2 * f; s.n_tiles_n = f / 128; s.b = w13; s.bs = w13_s;
+  s.f = f; s.h = h; s.hs = hs;
+  const int grid = ((num_cus_small() + 7) / 8) * 8;   // persistent: one workgroup per CU
+  hipLaunchKernelGGL(grouped_gemm_small_kernel<true>, dim3(grid), dim3(SM_THREADS), 0, stream, s, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_down_small(const uint8_t* h, const float* hs, const int32_t* offsets,
+                                  int n_groups, int total_rows, int d, int f, const uint8_t* w2,
+                                  const float* w2_s, uint16_t* y, hipStream_t stream) {
+  SmallArgs s{};
+  s.a = h; s.as = hs; s.a_rows = total_rows; s.row_src = nullptr; s.n_groups = n_groups;
+  s.total_rows = total_rows; s.K = f; s.N = d; s.n_tiles_n = (d + 255) / 256; s.b = w2; s.bs = w2_s;
+  s.f = f; s.y = y;
+  const int grid = ((num_cus_small() + 7) / 8) * 8;   // persistent: one workgroup per CU
+  hipLaunchKernelGGL(grouped_gemm_small_kernel<false>, dim3(grid), dim3(SM_THREADS), 0, stream, s, offsets);
+  return hipGetLastError();
+}
+
+}  // namespace moe

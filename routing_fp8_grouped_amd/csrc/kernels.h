@@ -32,6 +32,16 @@ hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* of
                             int total_rows, int d, int f, const uint8_t* w2, const float* w2_s,
                             uint16_t* y, hipStream_t stream);
 
+// Variants of the two expert GEMMs for few rows per group (weight streaming;
+// launch_gemm_up/down choose them when total_rows <= 16 * n_groups).
+hipError_t launch_gemm_up_small(const uint8_t* aq, const float* as, int a_rows,
+                                const int32_t* row_src, const int32_t* offsets, int n_groups,
+                                int total_rows, int d, int f, const uint8_t* w13,
+                                const float* w13_s, uint8_t* h, float* hs, hipStream_t stream);
+hipError_t launch_gemm_down_small(const uint8_t* h, const float* hs, const int32_t* offsets,
+                                  int n_groups, int total_rows, int d, int f, const uint8_t* w2,
+                                  const float* w2_s, uint16_t* y, hipStream_t stream);
+
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k,
                           int d, int shared_row0, uint16_t* out, hipStream_t stream);
 

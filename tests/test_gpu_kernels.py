@@ -217,7 +217,11 @@ def gemm_case(rng, counts, d, f, a_rows, gather):
     ([0, 1, 130, 128, 257, 0], 256, 128, True),
     ([3, 0, 200, 64], 384, 256, True),
     ([129, 5], 512, 384, False),
+    # at most 16 rows per group on average: the weight-streaming kernels
+    # (chunks of 16 rows, a partial 256-row block of W2 at d = 384)
     ([2, 1, 3], 7168, 2048, True),
+    ([0, 3, 16, 17, 1, 0], 384, 256, True),
+    ([5, 0, 2], 256, 128, False),
 ])
 def test_gemm_parity(counts, d, f, gather):
     log(f"grouped gemm counts={counts} d={d} f={f} gather={gather}")
