@@ -179,6 +179,21 @@ moe_status moe_combine(const uint16_t* y, const int32_t* pos, const float* w,
                        int T, int k, int d, int32_t shared_row0,
                        uint16_t* out, void* stream);
 
+/* moe_bias_update — one step of the auxiliary-loss-free balancing controller
+ * ("DeepSeek-V3: the recipe, and the interconnect that shaped it", section
+ * "Auxiliary-loss-free balancing"; summary page section 2; book chapter 8
+ * "V3's routing-only bias"): for every routed expert e < n_experts,
+ *   bias[e] -= gamma * sign(load[e] - mean load)
+ * with load[e] = offsets[e+1] - offsets[e] (moe_permute's array) and the mean
+ * taken over the n_experts routed experts (offsets[n_experts] assignments);
+ * an expert exactly at the mean keeps its bias.  The comparison is exact
+ * (integers), the update FP32 with one rounding.
+ *   offsets  [n_experts + 1 or more] int32 on the device
+ *   bias     [n_experts] FP32 on the device, updated in place
+ * MOE_ERR_INVALID_ARG: n_experts < 1, gamma not finite, misaligned pointers. */
+moe_status moe_bias_update(const int32_t* offsets, int n_experts, float gamma, float* bias,
+                           void* stream);
+
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 

@@ -17,7 +17,7 @@ from ._lib import MoEError, RouteParams  # noqa: F401
 
 __all__ = ["moe_route", "fp8_quant_1x128", "fp8_quant_128x128", "moe_permute_workspace_bytes",
            "moe_permute", "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up", "grouped_gemm_fp8_down",
-           "moe_combine", "MoEWeights", "MoELayer",
+           "moe_combine", "moe_bias_update", "MoEWeights", "MoELayer",
            "MoEError", "RouteParams"]
 
 
@@ -148,6 +148,18 @@ def moe_combine(y, pos, w, shared_row0, out, stream=None):
                                               shared_row0, _ptr(out), _stream(stream)))
 
 
+def moe_bias_update(offsets, bias, gamma, stream=None):
+    """Bias controller step: bias[e] -= gamma * sign(load[e] - mean load) for the
+    bias.numel() routed experts, loads from moe_permute's offsets."""
+    _dev(offsets, torch.int32, "offsets"); _dev(bias, torch.float32, "bias")
+    E = bias.numel()
+    if offsets.numel() < E + 1:
+        raise ValueError(f"offsets has {offsets.numel()} entries, {E + 1} needed")
+    lib = _lib.load()
+    _lib.check("moe_bias_update", lib.moe_bias_update(_ptr(offsets), E, float(gamma), _ptr(bias),
+                                                      _stream(stream)))
+
+
 class MoEWeights:
     """FP8 expert weights of one layer: w13 [E+1, 2f, d], w2 [E+1, d, f] E4M3
     with 128x128 block scales; index E is the shared expert."""
@@ -227,3 +239,8 @@ class MoELayer:
         moe_combine(self.y, self.pos, self.w, self.T * self.k, self.out, stream)
         mark("combine")
         return self.out
+
+    def update_bias(self, bias, gamma, stream=None):
+        """After forward(): one step of the balancing controller on ``bias``
+        [E] from this batch's expert loads (training-time only)."""
+        moe_bias_update(self.offsets, bias, gamma, stream)

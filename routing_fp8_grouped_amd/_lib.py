@@ -45,6 +45,7 @@ SIGNATURES = {
     "grouped_gemm_fp8_up": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P]),
     "grouped_gemm_fp8_down": (I, [P, P, P, I, I, I, I, P, P, P, P]),
     "moe_combine": (I, [P, P, P, I, I, I, ctypes.c_int32, P, P]),
+    "moe_bias_update": (I, [P, I, ctypes.c_float, P, P]),
     "moe_status_string": (ctypes.c_char_p, [I]),
     "moe_last_error": (ctypes.c_char_p, []),
 }

@@ -299,4 +299,16 @@ moe_status moe_combine(const uint16_t* y, const int32_t* pos, const float* w, in
                     "moe_combine launch");
 }
 
+moe_status moe_bias_update(const int32_t* offsets, int n_experts, float gamma, float* bias,
+                           void* stream) {
+  clear_error();
+  REQUIRE(n_experts >= 1, "n_experts=%d must be >= 1", n_experts);
+  REQUIRE(std::isfinite(gamma), "gamma is not finite");
+  REQUIRE_PTR4(offsets);
+  REQUIRE_PTR4(bias);
+  return hip_status(moe::launch_bias_update(offsets, n_experts, gamma, bias,
+                                            static_cast<hipStream_t>(stream)),
+                    "moe_bias_update launch");
+}
+
 }  // extern "C"

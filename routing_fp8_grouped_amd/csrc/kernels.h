@@ -42,6 +42,9 @@ hipError_t launch_gemm_down_small(const uint8_t* h, const float* hs, const int32
                                   int n_groups, int total_rows, int d, int f, const uint8_t* w2,
                                   const float* w2_s, uint16_t* y, hipStream_t stream);
 
+hipError_t launch_bias_update(const int32_t* offsets, int E, float gamma, float* bias,
+                              hipStream_t stream);
+
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k,
                           int d, int shared_row0, uint16_t* out, hipStream_t stream);
 

@@ -28,8 +28,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == {"moe_route", "fp8_quant_1x128", "fp8_quant_128x128",
                              "moe_permute_workspace_bytes", "moe_permute",
                              "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up",
-                             "grouped_gemm_fp8_down", "moe_combine", "moe_status_string",
-                             "moe_last_error"}
+                             "grouped_gemm_fp8_down", "moe_combine", "moe_bias_update",
+                             "moe_status_string", "moe_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -133,6 +133,13 @@ def test_combine_validation(lib):
     assert lib.moe_combine(A, A, A, 10, 8, 256, -2, A, None) == 1
     assert lib.moe_combine(A, None, A, 10, 8, 256, 80, A, None) == 1 and "pos is NULL" in last(lib)
     assert lib.moe_combine(None, None, None, 0, 8, 256, 0, None, None) == 0
+
+
+def test_bias_update_validation(lib):
+    assert lib.moe_bias_update(A, 0, 0.001, A, None) == 1
+    assert lib.moe_bias_update(A, 256, float("inf"), A, None) == 1 and "gamma" in last(lib)
+    assert lib.moe_bias_update(None, 256, 0.001, A, None) == 1 and "offsets is NULL" in last(lib)
+    assert lib.moe_bias_update(A, 256, 0.001, MIS4, None) == 1
 
 
 def test_error_is_thread_local(lib):
