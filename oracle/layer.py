@@ -21,6 +21,10 @@ Rounding points emulated (readings): the GEMM outputs G and U are rounded to
 FP32; h = fl32(SiLU(g) * u); each expert output is fl32 then BF16; the combine
 sums in float64 and rounds once to BF16.
 
+``rule`` selects the scale rule of every quantisation on the path ("fp32",
+the pages' amax/448, or "pow2", the power-of-two rule of ``oracle.quant``); the
+GEMMs use whatever scales the operands carry.
+
 Weight layout: w13[e] is [2f, d] with rows [0, f) = W1 (gate branch) and rows
 [f, 2f) = W3 (up branch); w2[e] is [d, f]; expert index E is the shared expert.
 """
@@ -44,21 +48,21 @@ def swiglu(g, u):
     return f32(silu(g) * np.asarray(u, np.float64))
 
 
-def quantize_expert(w13, w2):
+def quantize_expert(w13, w2, rule="fp32"):
     """Offline 128x128 quantisation of one expert's BF16 weights."""
-    w13q, w13s = quant_128x128(w13)
-    w2q, w2s = quant_128x128(w2)
+    w13q, w13s = quant_128x128(w13, rule)
+    w2q, w2s = quant_128x128(w2, rule)
     return w13q, w13s, w2q, w2s
 
 
-def expert_ffn(xq, xs, w13q, w13s, w2q, w2s):
+def expert_ffn(xq, xs, w13q, w13s, w2q, w2s, rule="fp32"):
     """One expert on its FP8 rows.  Returns (y BF16 values as float32 [rows, d],
     dict of intermediates: g, u, h (FP32), hq, hs (its 1x128 quantisation))."""
     f = w13q.shape[0] // 2
     gu = f32(blocked_gemm(xq, xs, w13q, w13s))
     g, u = gu[:, :f], gu[:, f:]
     h = swiglu(g, u)
-    hq, hs = quant_1x128(h)
+    hq, hs = quant_1x128(h, rule)
     y = bf16_round(f32(blocked_gemm(hq, hs, w2q, w2s)))
     return y, {"g": g, "u": u, "h": h, "hq": hq, "hs": hs}
 
@@ -71,7 +75,7 @@ def combine(y_routed, w, y_shared):
     return bf16_round(acc)
 
 
-def moe_layer(x, wg, bias, experts, n_groups, topk_groups, k, route_scale):
+def moe_layer(x, wg, bias, experts, n_groups, topk_groups, k, route_scale, rule="fp32"):
     """Whole-batch layer.  ``experts(e)`` returns the quantised weights
     (w13q, w13s, w2q, w2s) of expert e, e = 0..E (E = shared).
     Returns a dict with every intermediate of the path."""
@@ -79,7 +83,7 @@ def moe_layer(x, wg, bias, experts, n_groups, topk_groups, k, route_scale):
     T, d = x.shape
     E = np.asarray(wg).shape[0]
     r = route_tokens(x, wg, bias, n_groups, topk_groups, k, route_scale)
-    xq, xs = quant_1x128(x)
+    xq, xs = quant_1x128(x, rule)
     offsets, pos, row_token = permute(r["idx"], E)
     xq_perm = gather_rows(xq, row_token, T)
     xs_perm = gather_rows(xs, row_token, T)
@@ -97,7 +101,7 @@ def moe_layer(x, wg, bias, experts, n_groups, topk_groups, k, route_scale):
             hq = np.zeros((rows, f), np.uint8)
             hs = np.zeros((rows, f // 128), np.float32)
             g, u, h = (np.zeros((rows, f), np.float32) for _ in range(3))
-        ye, inter = expert_ffn(xq_perm[lo:hi], xs_perm[lo:hi], w13q, w13s, w2q, w2s)
+        ye, inter = expert_ffn(xq_perm[lo:hi], xs_perm[lo:hi], w13q, w13s, w2q, w2s, rule)
         y[lo:hi] = ye
         hq[lo:hi] = inter["hq"]
         hs[lo:hi] = inter["hs"]
@@ -109,7 +113,7 @@ def moe_layer(x, wg, bias, experts, n_groups, topk_groups, k, route_scale):
             "g": g, "u": u, "h": h, "hq": hq, "hs": hs, "y": y, "out": out}
 
 
-def moe_layer_tokens(x_rows, wg, bias, experts, n_groups, topk_groups, k, route_scale):
+def moe_layer_tokens(x_rows, wg, bias, experts, n_groups, topk_groups, k, route_scale, rule="fp32"):
     """Layer output for a set of tokens evaluated on their own.  Every step after
     routing acts on one token at a time (1x128 tiles lie within a row, experts act
     row-wise, the combine is per token) and routing is per token, so this equals
@@ -121,7 +125,7 @@ def moe_layer_tokens(x_rows, wg, bias, experts, n_groups, topk_groups, k, route_
     n, d = x_rows.shape
     E = np.asarray(wg).shape[0]
     r = route_tokens(x_rows, wg, bias, n_groups, topk_groups, k, route_scale)
-    xq, xs = quant_1x128(x_rows)
+    xq, xs = quant_1x128(x_rows, rule)
     y_routed = np.zeros((n, k, d), np.float32)
     y_shared = np.zeros((n, d), np.float32)
     need = {}
@@ -132,12 +136,12 @@ def moe_layer_tokens(x_rows, wg, bias, experts, n_groups, topk_groups, k, route_
     for e in sorted(need):
         w13q, w13s, w2q, w2s = experts(e)
         ts = [t for t, _ in need[e]]
-        ye, inter = expert_ffn(xq[ts], xs[ts], w13q, w13s, w2q, w2s)
+        ye, inter = expert_ffn(xq[ts], xs[ts], w13q, w13s, w2q, w2s, rule)
         for i, ((t, j), row) in enumerate(zip(need[e], ye)):
             y_routed[t, j] = row
             inter_routed[(t, j)] = {key: val[i:i + 1] for key, val in inter.items()}
     w13q, w13s, w2q, w2s = experts(E)
-    y_shared[:], inter = expert_ffn(xq, xs, w13q, w13s, w2q, w2s)
+    y_shared[:], inter = expert_ffn(xq, xs, w13q, w13s, w2q, w2s, rule)
     for t in range(n):
         inter_shared[t] = {key: val[t:t + 1] for key, val in inter.items()}
     extra = {"xq": xq, "xs": xs, "y_routed": y_routed, "y_shared": y_shared,
