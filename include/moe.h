@@ -194,6 +194,41 @@ moe_status moe_combine(const uint16_t* y, const int32_t* pos, const float* w,
 moe_status moe_bias_update(const int32_t* offsets, int n_experts, float gamma, float* bias,
                            void* stream);
 
+/* ---- Power-of-two (E8M0) scale variant ----
+ * The pages' training recipe uses power-of-two scaling factors for some
+ * tensors (summary page section 6; book chapter 17), and block-scaled matrix
+ * hardware takes one 8-bit exponent per block (summary page section 6,
+ * microscaling).  In this variant every scale is the smallest power of two
+ * not below fl32(amax/448), at least 2^-127, 1.0 for an all-zero tile; it is
+ * stored as that FP32 value in the same arrays as above, so its FP32 exponent
+ * field is its E8M0 code.  Codes are E4M3(fl32(x / scale)) as before.  With
+ * such scales the GEMMs pass the scales to gfx950's block-scaled MFMA and
+ * accumulate in the instruction (no software promotion). */
+
+/* fp8_quant_1x128_pow2 / fp8_quant_128x128_pow2 — fp8_quant_1x128 and
+ * fp8_quant_128x128 with the power-of-two scale rule; same arguments, layouts
+ * and errors. */
+moe_status fp8_quant_1x128_pow2(const uint16_t* x, int rows, int cols,
+                                uint8_t* q, float* scale, void* stream);
+moe_status fp8_quant_128x128_pow2(const uint16_t* w, int N, int K,
+                                  uint8_t* q, float* scale, void* stream);
+
+/* grouped_gemm_fp8_up_e8m0 / grouped_gemm_fp8_down_e8m0 — grouped_gemm_fp8_up
+ * and grouped_gemm_fp8_down for operands whose every scale (as, w13_s, hs,
+ * w2_s) is a power of two in [2^-127, 2^127], as the _pow2 quantisers write
+ * them; h is requantised with the power-of-two rule.  Same arguments, layouts
+ * and errors.  A scale that is not such a power of two is read as its FP32
+ * exponent only (the result is then wrong; it is not checked). */
+moe_status grouped_gemm_fp8_up_e8m0(const uint8_t* aq, const float* as, int a_rows,
+                                    const int32_t* row_src, const int32_t* offsets,
+                                    int n_groups, int total_rows, int d, int f,
+                                    const uint8_t* w13, const float* w13_s,
+                                    uint8_t* h, float* hs, void* stream);
+moe_status grouped_gemm_fp8_down_e8m0(const uint8_t* h, const float* hs, const int32_t* offsets,
+                                      int n_groups, int total_rows, int d, int f,
+                                      const uint8_t* w2, const float* w2_s,
+                                      uint16_t* y, void* stream);
+
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 

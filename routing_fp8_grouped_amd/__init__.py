@@ -17,7 +17,8 @@ from ._lib import MoEError, RouteParams  # noqa: F401
 
 __all__ = ["moe_route", "fp8_quant_1x128", "fp8_quant_128x128", "moe_permute_workspace_bytes",
            "moe_permute", "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up", "grouped_gemm_fp8_down",
-           "moe_combine", "moe_bias_update", "MoEWeights", "MoELayer",
+           "moe_combine", "moe_bias_update", "fp8_quant_1x128_pow2", "fp8_quant_128x128_pow2",
+           "grouped_gemm_fp8_up_e8m0", "grouped_gemm_fp8_down_e8m0", "MoEWeights", "MoELayer",
            "MoEError", "RouteParams"]
 
 
@@ -52,23 +53,39 @@ def moe_route(x, wg, bias, n_groups, topk_groups, topk, route_scale, idx, w, str
                                           _stream(stream)))
 
 
-def fp8_quant_1x128(x, q, scale, stream=None):
-    """x [rows, cols] BF16 -> q [rows, cols] uint8 E4M3, scale [rows, cols/128] float32."""
+def _quant_1x128(name, x, q, scale, stream):
     _dev(x, torch.bfloat16, "x"); _dev(q, torch.uint8, "q"); _dev(scale, torch.float32, "scale")
     rows, cols = x.shape
-    lib = _lib.load()
-    _lib.check("fp8_quant_1x128", lib.fp8_quant_1x128(_ptr(x), rows, cols, _ptr(q), _ptr(scale),
-                                                      _stream(stream)))
+    fn = getattr(_lib.load(), name)
+    _lib.check(name, fn(_ptr(x), rows, cols, _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def _quant_128x128(name, w, q, scale, stream):
+    _dev(w, torch.bfloat16, "w"); _dev(q, torch.uint8, "q"); _dev(scale, torch.float32, "scale")
+    K = w.shape[-1]
+    N = w.numel() // K
+    fn = getattr(_lib.load(), name)
+    _lib.check(name, fn(_ptr(w), N, K, _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def fp8_quant_1x128(x, q, scale, stream=None):
+    """x [rows, cols] BF16 -> q [rows, cols] uint8 E4M3, scale [rows, cols/128] float32."""
+    _quant_1x128("fp8_quant_1x128", x, q, scale, stream)
+
+
+def fp8_quant_1x128_pow2(x, q, scale, stream=None):
+    """fp8_quant_1x128 with power-of-two scales."""
+    _quant_1x128("fp8_quant_1x128_pow2", x, q, scale, stream)
 
 
 def fp8_quant_128x128(w, q, scale, stream=None):
     """w [..., N, K] BF16 (leading dims folded into N) -> q uint8, scale [..., N/128, K/128]."""
-    _dev(w, torch.bfloat16, "w"); _dev(q, torch.uint8, "q"); _dev(scale, torch.float32, "scale")
-    K = w.shape[-1]
-    N = w.numel() // K
-    lib = _lib.load()
-    _lib.check("fp8_quant_128x128", lib.fp8_quant_128x128(_ptr(w), N, K, _ptr(q), _ptr(scale),
-                                                          _stream(stream)))
+    _quant_128x128("fp8_quant_128x128", w, q, scale, stream)
+
+
+def fp8_quant_128x128_pow2(w, q, scale, stream=None):
+    """fp8_quant_128x128 with power-of-two scales."""
+    _quant_128x128("fp8_quant_128x128_pow2", w, q, scale, stream)
 
 
 def moe_permute_workspace_bytes(T, k, E):
@@ -111,31 +128,49 @@ def grouped_gemm_fp8_swiglu(aq, as_, row_src, offsets, w13, w13_s, w2, w2_s, h, 
         _stream(stream)))
 
 
-def grouped_gemm_fp8_up(aq, as_, row_src, offsets, w13, w13_s, h, hs, stream=None):
-    """First expert GEMM with the SwiGLU epilogue: h/hs [rows, f]."""
+def _gemm_up(name, aq, as_, row_src, offsets, w13, w13_s, h, hs, stream):
     for t, dt, n in ((aq, torch.uint8, "aq"), (as_, torch.float32, "as"),
                      (row_src, torch.int32, "row_src"), (offsets, torch.int32, "offsets"),
                      (w13, torch.uint8, "w13"), (w13_s, torch.float32, "w13_s"),
                      (h, torch.uint8, "h"), (hs, torch.float32, "hs")):
         _dev(t, dt, n)
     n_groups, two_f, d = w13.shape
-    lib = _lib.load()
-    _lib.check("grouped_gemm_fp8_up", lib.grouped_gemm_fp8_up(
+    fn = getattr(_lib.load(), name)
+    _lib.check(name, fn(
         _ptr(aq), _ptr(as_), aq.shape[0], _ptr(row_src), _ptr(offsets), n_groups, h.shape[0], d,
         two_f // 2, _ptr(w13), _ptr(w13_s), _ptr(h), _ptr(hs), _stream(stream)))
 
 
-def grouped_gemm_fp8_down(h, hs, offsets, w2, w2_s, y, stream=None):
-    """Second expert GEMM: y [rows, d] BF16."""
+def grouped_gemm_fp8_up(aq, as_, row_src, offsets, w13, w13_s, h, hs, stream=None):
+    """First expert GEMM with the SwiGLU epilogue: h/hs [rows, f]."""
+    _gemm_up("grouped_gemm_fp8_up", aq, as_, row_src, offsets, w13, w13_s, h, hs, stream)
+
+
+def grouped_gemm_fp8_up_e8m0(aq, as_, row_src, offsets, w13, w13_s, h, hs, stream=None):
+    """grouped_gemm_fp8_up for power-of-two scales (hardware block-scaled MFMA)."""
+    _gemm_up("grouped_gemm_fp8_up_e8m0", aq, as_, row_src, offsets, w13, w13_s, h, hs, stream)
+
+
+def _gemm_down(name, h, hs, offsets, w2, w2_s, y, stream):
     for t, dt, n in ((h, torch.uint8, "h"), (hs, torch.float32, "hs"),
                      (offsets, torch.int32, "offsets"), (w2, torch.uint8, "w2"),
                      (w2_s, torch.float32, "w2_s"), (y, torch.bfloat16, "y")):
         _dev(t, dt, n)
     n_groups, d, f = w2.shape
-    lib = _lib.load()
-    _lib.check("grouped_gemm_fp8_down", lib.grouped_gemm_fp8_down(
+    fn = getattr(_lib.load(), name)
+    _lib.check(name, fn(
         _ptr(h), _ptr(hs), _ptr(offsets), n_groups, h.shape[0], d, f, _ptr(w2), _ptr(w2_s),
         _ptr(y), _stream(stream)))
+
+
+def grouped_gemm_fp8_down(h, hs, offsets, w2, w2_s, y, stream=None):
+    """Second expert GEMM: y [rows, d] BF16."""
+    _gemm_down("grouped_gemm_fp8_down", h, hs, offsets, w2, w2_s, y, stream)
+
+
+def grouped_gemm_fp8_down_e8m0(h, hs, offsets, w2, w2_s, y, stream=None):
+    """grouped_gemm_fp8_down for power-of-two scales (hardware block-scaled MFMA)."""
+    _gemm_down("grouped_gemm_fp8_down_e8m0", h, hs, offsets, w2, w2_s, y, stream)
 
 
 def moe_combine(y, pos, w, shared_row0, out, stream=None):
@@ -176,10 +211,12 @@ class MoEWeights:
                    torch.empty(n_groups, d, f, dtype=torch.uint8, device=device),
                    torch.empty(n_groups, d // 128, f // 128, dtype=torch.float32, device=device))
 
-    def quantize_expert(self, e, w13_bf16, w2_bf16, stream=None):
-        """Offline 128x128 quantisation of expert e's BF16 weights into place."""
-        fp8_quant_128x128(w13_bf16, self.w13q[e], self.w13s[e], stream)
-        fp8_quant_128x128(w2_bf16, self.w2q[e], self.w2s[e], stream)
+    def quantize_expert(self, e, w13_bf16, w2_bf16, stream=None, pow2=False):
+        """Offline 128x128 quantisation of expert e's BF16 weights into place
+        (power-of-two scales when ``pow2``)."""
+        q = fp8_quant_128x128_pow2 if pow2 else fp8_quant_128x128
+        q(w13_bf16, self.w13q[e], self.w13s[e], stream)
+        q(w2_bf16, self.w2q[e], self.w2s[e], stream)
 
 
 class MoELayer:
@@ -188,10 +225,17 @@ class MoELayer:
 
     With ``dispatch=False`` (default) the permute produces only the metadata and
     the first GEMM reads each token's FP8 row through row_token; with
-    ``dispatch=True`` the rows are first copied into grouped order."""
+    ``dispatch=True`` the rows are first copied into grouped order.
+
+    ``scales="pow2"`` runs the power-of-two scale variant: X and H get
+    power-of-two scales and the GEMMs use the hardware block-scaled MFMA (the
+    weights must then be quantised with ``pow2=True``)."""
 
     def __init__(self, T, d, E, n_groups, topk_groups, topk, f, route_scale=2.5, device="cuda",
-                 dispatch=False):
+                 dispatch=False, scales="fp32"):
+        if scales not in ("fp32", "pow2"):
+            raise ValueError(f"scales={scales!r} must be 'fp32' or 'pow2'")
+        self.pow2 = scales == "pow2"
         self.T, self.d, self.E, self.k, self.f = T, d, E, topk, f
         self.n_groups, self.topk_groups, self.route_scale = n_groups, topk_groups, route_scale
         self.dispatch = dispatch
@@ -219,7 +263,7 @@ class MoELayer:
         moe_route(x, wg, bias, self.n_groups, self.topk_groups, self.k, self.route_scale,
                   self.idx, self.w, stream)
         mark("route")
-        fp8_quant_1x128(x, self.xq, self.xs, stream)
+        (fp8_quant_1x128_pow2 if self.pow2 else fp8_quant_1x128)(x, self.xq, self.xs, stream)
         mark("quant")
         if self.dispatch:
             moe_permute(self.idx, self.E, self.offsets, self.pos, self.row_token, self.ws,
@@ -230,11 +274,11 @@ class MoELayer:
                         stream=stream)
             aq, as_, src = self.xq, self.xs, self.row_token
         mark("permute")
-        grouped_gemm_fp8_up(aq, as_, src, self.offsets, weights.w13q, weights.w13s, self.h,
-                            self.hs, stream)
+        up = grouped_gemm_fp8_up_e8m0 if self.pow2 else grouped_gemm_fp8_up
+        down = grouped_gemm_fp8_down_e8m0 if self.pow2 else grouped_gemm_fp8_down
+        up(aq, as_, src, self.offsets, weights.w13q, weights.w13s, self.h, self.hs, stream)
         mark("gemm_up")
-        grouped_gemm_fp8_down(self.h, self.hs, self.offsets, weights.w2q, weights.w2s, self.y,
-                              stream)
+        down(self.h, self.hs, self.offsets, weights.w2q, weights.w2s, self.y, stream)
         mark("gemm_down")
         moe_combine(self.y, self.pos, self.w, self.T * self.k, self.out, stream)
         mark("combine")

@@ -46,6 +46,10 @@ SIGNATURES = {
     "grouped_gemm_fp8_down": (I, [P, P, P, I, I, I, I, P, P, P, P]),
     "moe_combine": (I, [P, P, P, I, I, I, ctypes.c_int32, P, P]),
     "moe_bias_update": (I, [P, I, ctypes.c_float, P, P]),
+    "fp8_quant_1x128_pow2": (I, [P, I, I, P, P, P]),
+    "fp8_quant_128x128_pow2": (I, [P, I, I, P, P, P]),
+    "grouped_gemm_fp8_up_e8m0": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P]),
+    "grouped_gemm_fp8_down_e8m0": (I, [P, P, P, I, I, I, I, P, P, P, P]),
     "moe_status_string": (ctypes.c_char_p, [I]),
     "moe_last_error": (ctypes.c_char_p, []),
 }

@@ -115,22 +115,23 @@ moe_status moe_route(const uint16_t* x, const uint16_t* wg, const float* bias, i
                     "moe_route launch");
 }
 
-moe_status fp8_quant_1x128(const uint16_t* x, int rows, int cols, uint8_t* q, float* scale,
-                           void* stream) {
-  clear_error();
+namespace {
+
+moe_status quant_1x128_impl(const uint16_t* x, int rows, int cols, uint8_t* q, float* scale, bool pow2,
+                            void* stream) {
   REQUIRE(rows >= 0, "rows=%d is negative", rows);
   REQUIRE(cols >= 128 && cols % 128 == 0, "cols=%d must be a positive multiple of 128", cols);
   if (rows == 0) return MOE_OK;
   REQUIRE_PTR(x);
   REQUIRE_PTR(q);
   REQUIRE_PTR4(scale);
-  return hip_status(moe::launch_quant_1x128(x, rows, cols, q, scale, static_cast<hipStream_t>(stream)),
-                    "fp8_quant_1x128 launch");
+  return hip_status(moe::launch_quant_1x128(x, rows, cols, q, scale, pow2,
+                                            static_cast<hipStream_t>(stream)),
+                    pow2 ? "fp8_quant_1x128_pow2 launch" : "fp8_quant_1x128 launch");
 }
 
-moe_status fp8_quant_128x128(const uint16_t* w, int N, int K, uint8_t* q, float* scale,
-                             void* stream) {
-  clear_error();
+moe_status quant_128x128_impl(const uint16_t* w, int N, int K, uint8_t* q, float* scale, bool pow2,
+                              void* stream) {
   REQUIRE(N >= 0 && N % 128 == 0, "N=%d must be a non-negative multiple of 128", N);
   REQUIRE(K >= 128 && K % 128 == 0, "K=%d must be a positive multiple of 128", K);
   if (N == 0) return MOE_OK;
@@ -138,8 +139,35 @@ moe_status fp8_quant_128x128(const uint16_t* w, int N, int K, uint8_t* q, float*
   REQUIRE_PTR(w);
   REQUIRE_PTR(q);
   REQUIRE_PTR4(scale);
-  return hip_status(moe::launch_quant_128x128(w, N, K, q, scale, static_cast<hipStream_t>(stream)),
-                    "fp8_quant_128x128 launch");
+  return hip_status(moe::launch_quant_128x128(w, N, K, q, scale, pow2,
+                                              static_cast<hipStream_t>(stream)),
+                    pow2 ? "fp8_quant_128x128_pow2 launch" : "fp8_quant_128x128 launch");
+}
+
+}  // namespace
+
+moe_status fp8_quant_1x128(const uint16_t* x, int rows, int cols, uint8_t* q, float* scale,
+                           void* stream) {
+  clear_error();
+  return quant_1x128_impl(x, rows, cols, q, scale, false, stream);
+}
+
+moe_status fp8_quant_1x128_pow2(const uint16_t* x, int rows, int cols, uint8_t* q, float* scale,
+                                void* stream) {
+  clear_error();
+  return quant_1x128_impl(x, rows, cols, q, scale, true, stream);
+}
+
+moe_status fp8_quant_128x128(const uint16_t* w, int N, int K, uint8_t* q, float* scale,
+                             void* stream) {
+  clear_error();
+  return quant_128x128_impl(w, N, K, q, scale, false, stream);
+}
+
+moe_status fp8_quant_128x128_pow2(const uint16_t* w, int N, int K, uint8_t* q, float* scale,
+                                  void* stream) {
+  clear_error();
+  return quant_128x128_impl(w, N, K, q, scale, true, stream);
 }
 
 size_t moe_permute_workspace_bytes(int T, int k, int E) {
@@ -230,6 +258,31 @@ moe_status check_down(const uint8_t* h, const float* hs, const int32_t* offsets,
   return MOE_OK;
 }
 
+moe_status gemm_up_impl(const uint8_t* aq, const float* as, int a_rows, const int32_t* row_src,
+                        const int32_t* offsets, int n_groups, int total_rows, int d, int f,
+                        const uint8_t* w13, const float* w13_s, uint8_t* h, float* hs, bool e8m0,
+                        void* stream) {
+  moe_status s = check_gemm_shape(n_groups, total_rows, d, f);
+  if (s != MOE_OK || total_rows == 0) return s;
+  s = check_up(d, aq, as, a_rows, row_src, offsets, total_rows, w13, w13_s, h, hs);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_gemm_up(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d,
+                                        f, w13, w13_s, h, hs, e8m0, static_cast<hipStream_t>(stream)),
+                    e8m0 ? "grouped_gemm_fp8_up_e8m0 launch" : "grouped_gemm_fp8_up launch");
+}
+
+moe_status gemm_down_impl(const uint8_t* h, const float* hs, const int32_t* offsets, int n_groups,
+                          int total_rows, int d, int f, const uint8_t* w2, const float* w2_s,
+                          uint16_t* y, bool e8m0, void* stream) {
+  moe_status s = check_gemm_shape(n_groups, total_rows, d, f);
+  if (s != MOE_OK || total_rows == 0) return s;
+  s = check_down(h, hs, offsets, w2, w2_s, y);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_gemm_down(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y,
+                                          e8m0, static_cast<hipStream_t>(stream)),
+                    e8m0 ? "grouped_gemm_fp8_down_e8m0 launch" : "grouped_gemm_fp8_down launch");
+}
+
 }  // namespace
 
 moe_status grouped_gemm_fp8_up(const uint8_t* aq, const float* as, int a_rows,
@@ -237,26 +290,31 @@ moe_status grouped_gemm_fp8_up(const uint8_t* aq, const float* as, int a_rows,
                                int total_rows, int d, int f, const uint8_t* w13,
                                const float* w13_s, uint8_t* h, float* hs, void* stream) {
   clear_error();
-  moe_status s = check_gemm_shape(n_groups, total_rows, d, f);
-  if (s != MOE_OK || total_rows == 0) return s;
-  s = check_up(d, aq, as, a_rows, row_src, offsets, total_rows, w13, w13_s, h, hs);
-  if (s != MOE_OK) return s;
-  return hip_status(moe::launch_gemm_up(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d,
-                                        f, w13, w13_s, h, hs, static_cast<hipStream_t>(stream)),
-                    "grouped_gemm_fp8_up launch");
+  return gemm_up_impl(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d, f, w13, w13_s, h,
+                      hs, false, stream);
+}
+
+moe_status grouped_gemm_fp8_up_e8m0(const uint8_t* aq, const float* as, int a_rows,
+                                    const int32_t* row_src, const int32_t* offsets, int n_groups,
+                                    int total_rows, int d, int f, const uint8_t* w13,
+                                    const float* w13_s, uint8_t* h, float* hs, void* stream) {
+  clear_error();
+  return gemm_up_impl(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d, f, w13, w13_s, h,
+                      hs, true, stream);
 }
 
 moe_status grouped_gemm_fp8_down(const uint8_t* h, const float* hs, const int32_t* offsets,
                                  int n_groups, int total_rows, int d, int f, const uint8_t* w2,
                                  const float* w2_s, uint16_t* y, void* stream) {
   clear_error();
-  moe_status s = check_gemm_shape(n_groups, total_rows, d, f);
-  if (s != MOE_OK || total_rows == 0) return s;
-  s = check_down(h, hs, offsets, w2, w2_s, y);
-  if (s != MOE_OK) return s;
-  return hip_status(moe::launch_gemm_down(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y,
-                                          static_cast<hipStream_t>(stream)),
-                    "grouped_gemm_fp8_down launch");
+  return gemm_down_impl(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y, false, stream);
+}
+
+moe_status grouped_gemm_fp8_down_e8m0(const uint8_t* h, const float* hs, const int32_t* offsets,
+                                      int n_groups, int total_rows, int d, int f, const uint8_t* w2,
+                                      const float* w2_s, uint16_t* y, void* stream) {
+  clear_error();
+  return gemm_down_impl(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y, true, stream);
 }
 
 moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, int a_rows,
@@ -273,11 +331,11 @@ moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, int a_row
   if (s != MOE_OK) return s;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   s = hip_status(moe::launch_gemm_up(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d, f,
-                                     w13, w13_s, h, hs, st),
+                                     w13, w13_s, h, hs, false, st),
                  "grouped_gemm_fp8_swiglu launch (up)");
   if (s != MOE_OK) return s;
   return hip_status(moe::launch_gemm_down(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y,
-                                          st),
+                                          false, st),
                     "grouped_gemm_fp8_swiglu launch (down)");
 }
 

@@ -49,12 +49,36 @@ __device__ __forceinline__ float scale_from_amax(float amax) {
   return amax == 0.0f ? 1.0f : amax / kE4M3Max;
 }
 
+// Power-of-two scale: the smallest power of two not below fl32(amax/448), at
+// least 2^-127 (the smallest E8M0 value, an FP32 subnormal); 1.0 for an
+// all-zero tile.  Its FP32 exponent field is the E8M0 code of the scale.
+__device__ __forceinline__ float scale_from_amax_pow2(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  const uint32_t b = __float_as_uint(amax / kE4M3Max);
+  if (b <= 0x00400000u) return __uint_as_float(0x00400000u);   // at most 2^-127
+  if (b < 0x00800000u) return __uint_as_float(0x00800000u);    // other subnormals: 2^-126
+  return (b & 0x007FFFFFu) ? __uint_as_float((b & 0x7F800000u) + 0x00800000u) : __uint_as_float(b);
+}
+
+template <bool POW2>
+__device__ __forceinline__ float tile_scale(float amax) {
+  return POW2 ? scale_from_amax_pow2(amax) : scale_from_amax(amax);
+}
+
 // One 16x16x128 FP8 E4M3 MFMA: D = A * B^T + C.  Lane l supplies row l%16 of A
 // (and row l%16 of B, i.e. column l%16 of the product) with the 32 K-values
 // [(l/16)*32, (l/16)*32 + 32); D holds rows (l/16)*4 + i, column l%16.  The
 // E8M0 block scales are fixed at 2^0 (code 127).
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// The same MFMA with hardware block scales: D = (2^(ea-127) A) * (2^(eb-127) B)^T
+// + C, where byte 0 of `ea` is the E8M0 code of the scale of the row (of A)
+// that the lane supplies and byte 0 of `eb` that of the lane's B row (column
+// of the product); each lane's code covers its own 32 K-values.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128_scaled(v8i a, v8i b, v4f c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
 
 // 16x16x32 BF16 MFMA with the same row/column conventions; lane l holds the 8

@@ -29,6 +29,12 @@
 // refilled with the block two ahead, and the first fragments of the next block
 // are read while the last MFMAs of this block run.
 //
+// Power-of-two variant (E8M0): when every activation, weight and H scale is a
+// power of two (the quantisers' power-of-two rule), the scales go into the
+// instruction's hardware block-scale operands (the E8M0 code is the FP32
+// exponent field) and the accumulator is chained through the MFMA: no partial
+// sums, no promotion FMAs.  H is then requantised with the same rule.
+//
 // Work distribution: the tile list (group, m super-block of 4 m-tiles, n-tile,
 // m-tile) is built on the device from the group offsets, so nothing waits on
 // the host for the ragged row counts.  Workgroup b runs on XCD b % 8 and takes
@@ -239,7 +245,7 @@ __device__ __forceinline__ float div_by(float x, float s, float r) {
 // replaces g (WN = 0) or u (WN = 1) in the accumulator.  Then the 1x128 amax
 // is combined across the pair through smAmax, and the E4M3 codes are staged
 // for 16-byte stores.
-template <int WN>
+template <int WN, bool POW2>
 __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& p, const Tile& cur, v4f (&acc)[4][8],
                                                 unsigned char* E, float (*smAmax)[BM], int wave,
                                                 int wm, int lane) {
@@ -293,7 +299,7 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& p, const Tile& c
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int rt = wm * 64 + (2 * r + msl) * 16 + g16 * 4 + e;
-        const float sc = scale_from_amax(fmaxf(smAmax[0][rt], smAmax[1][rt]));
+        const float sc = tile_scale<POW2>(fmaxf(smAmax[0][rt], smAmax[1][rt]));
         const float rs = recip(sc);
         if (WN == 0 && r16 == 0 && rt < cur.rows_valid) p.hs[(size_t)(cur.row0 + rt) * nhs + cur.n] = sc;
 #pragma unroll
@@ -392,10 +398,21 @@ struct Frags {
   v8i af[4];       // activation fragments of the block (rows ms*16 .. +15)
   v8i bq[2];       // weight fragments, column ns in slot ns & 1
   float cs[4][4];  // activation scale x weight scale of this lane's 16 rows
+  int ea[4];       // E8M0 variant: scale code of this lane's A row of fragment ms
+  int eb;          // E8M0 variant: scale code of the wave's weight block
 };
 
-__device__ __forceinline__ void load_scales(Frags& F, const unsigned char* stage, int wm, int wn, int g16) {
+template <bool E8M0>
+__device__ __forceinline__ void load_scales(Frags& F, const unsigned char* stage, int wm, int wn, int g16,
+                                            int r16) {
   const unsigned char* B_ = stage + ST_A;
+  if (E8M0) {
+    const uint32_t* SA_ = reinterpret_cast<const uint32_t*>(B_ + ST_B);
+    F.eb = (int)(reinterpret_cast<const uint32_t*>(B_ + ST_B + ST_SA)[wn] >> 23);
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) F.ea[ms] = (int)(SA_[wm * 64 + ms * 16 + r16] >> 23);
+    return;
+  }
   const float* SA_ = reinterpret_cast<const float*>(B_ + ST_B);
   const float sw = reinterpret_cast<const float*>(B_ + ST_B + ST_SA)[wn];
 #pragma unroll
@@ -408,12 +425,13 @@ __device__ __forceinline__ void load_scales(Frags& F, const unsigned char* stage
   }
 }
 
+template <bool E8M0>
 __device__ __forceinline__ void load_first(Frags& F, const unsigned char* stage, int wm, int wn, int g16,
                                            int r16) {
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms) F.af[ms] = frag(stage, wm * 64 + ms * 16 + r16, g16);
   F.bq[0] = frag(stage + ST_A, wn * 128 + r16, g16);
-  load_scales(F, stage, wm, wn, g16);
+  load_scales<E8M0>(F, stage, wm, wn, g16, r16);
 }
 
 // One K block on stage `cur`: MFMA i = (ns, ms) in ns-major order, each
@@ -425,7 +443,9 @@ __device__ __forceinline__ void load_first(Frags& F, const unsigned char* stage,
 //
 // A wave whose 64 rows all lie past the end of a partial tile (`active` false)
 // skips the reads and the arithmetic but keeps the barrier and the loads.
-template <bool SWIGLU, bool LAST>
+//
+// E8M0: the MFMA takes the block scales and accumulates into acc directly.
+template <bool SWIGLU, bool LAST, bool E8M0>
 __device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGLU>& ld,
                                         unsigned char* cur, const unsigned char* nxt, int wm, int wn,
                                         int g16, int r16, bool active) {
@@ -453,8 +473,16 @@ __device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGL
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) {
       const int i = ns * 4 + ms;
-      part[i & 1] = mfma_fp8_16x16x128(F.af[ms], F.bq[ns & 1], v4f{0.f, 0.f, 0.f, 0.f});
-      if (i >= 1) {
+      if (E8M0) {
+        acc[ms][ns] = mfma_fp8_16x16x128_scaled(F.af[ms], F.bq[ns & 1], acc[ms][ns], F.ea[ms], F.eb);
+        if (i >= 1) {
+          const int pi = i - 1;
+          asm volatile("" : "+v"(acc[pi & 3][pi >> 2]));
+        }
+      } else {
+        part[i & 1] = mfma_fp8_16x16x128(F.af[ms], F.bq[ns & 1], v4f{0.f, 0.f, 0.f, 0.f});
+      }
+      if (!E8M0 && i >= 1) {
         const int pi = i - 1, pms = pi & 3, pns = pi >> 2;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -472,12 +500,13 @@ __device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGL
       }
     }
   }
+  if (!E8M0)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc[3][7][e] = fmaf(part[1][e], F.cs[3][e], acc[3][7][e]);
-  if (!LAST) load_scales(F, nxt, wm, wn, g16);
+    for (int e = 0; e < 4; ++e) acc[3][7][e] = fmaf(part[1][e], F.cs[3][e], acc[3][7][e]);
+  if (!LAST) load_scales<E8M0>(F, nxt, wm, wn, g16, r16);
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool E8M0>
 __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_kernel(GemmArgs p,
                                                               const int32_t* __restrict__ offsets) {
   __shared__ __attribute__((aligned(16))) unsigned char sm[2 * STG];
@@ -543,19 +572,19 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_kernel(GemmArgs p,
       for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = v4f{0.f, 0.f, 0.f, 0.f};
     // rows wm*64 .. +63 hold data (uniform per wave)
     const bool active = wm * 64 < cur.rows_valid;
-    if (active) load_first(F, sm + S * STG, wm, wn, g16, r16);
+    if (active) load_first<E8M0>(F, sm + S * STG, wm, wn, g16, r16);
     for (int kb = 0; kb < KB - 1; ++kb) {
-      k_block<SWIGLU, false>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16, active);
+      k_block<SWIGLU, false, E8M0>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16, active);
       S ^= 1;
     }
-    k_block<SWIGLU, true>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16, active);
+    k_block<SWIGLU, true, E8M0>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16, active);
 
     // ---- epilogue, through stage S (every wave has finished reading it: the
     // ring barrier of the last block followed the last read) ----
     unsigned char* E = sm + S * STG;
     if (SWIGLU) {
-      if (wn == 0) epilogue_swiglu<0>(p, cur, acc, E, smAmax, wave, wm, lane);
-      else epilogue_swiglu<1>(p, cur, acc, E, smAmax, wave, wm, lane);
+      if (wn == 0) epilogue_swiglu<0, E8M0>(p, cur, acc, E, smAmax, wave, wm, lane);
+      else epilogue_swiglu<1, E8M0>(p, cur, acc, E, smAmax, wave, wm, lane);
     } else {
       epilogue_bf16(p, cur, acc, E, wave, wm, wn, lane);
     }
@@ -584,10 +613,10 @@ static int num_cus() {
 hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const int32_t* row_src,
                           const int32_t* offsets, int n_groups, int total_rows, int d, int f,
                           const uint8_t* w13, const float* w13_s, uint8_t* h, float* hs,
-                          hipStream_t stream) {
+                          bool e8m0, hipStream_t stream) {
   if (total_rows <= 16 * n_groups)   // few rows per group: stream the weights
     return launch_gemm_up_small(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d, f, w13,
-                                w13_s, h, hs, stream);
+                                w13_s, h, hs, e8m0, stream);
   const int grid = ((num_cus() + 7) / 8) * 8;
   GemmArgs s1{};
   s1.a = aq;
@@ -604,13 +633,18 @@ hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const 
   s1.f = f;
   s1.h = h;
   s1.hs = hs;
-  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(grid), dim3(NTHR), 0, stream, s1, offsets);
+  if (e8m0)
+    hipLaunchKernelGGL((grouped_gemm_kernel<true, true>), dim3(grid), dim3(NTHR), 0, stream, s1, offsets);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<true, false>), dim3(grid), dim3(NTHR), 0, stream, s1, offsets);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* offsets, int n_groups,
                             int total_rows, int d, int f, const uint8_t* w2, const float* w2_s,
-                            uint16_t* y, hipStream_t stream) {
+                            uint16_t* y, bool e8m0, hipStream_t stream) {
+  // few rows per group: the weight-streaming kernel, whose software promotion
+  // is exact with power-of-two scales
   if (total_rows <= 16 * n_groups)
     return launch_gemm_down_small(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y, stream);
   const int grid = ((num_cus() + 7) / 8) * 8;
@@ -628,7 +662,10 @@ hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* of
   s2.bs = w2_s;
   s2.f = f;
   s2.y = y;
-  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(grid), dim3(NTHR), 0, stream, s2, offsets);
+  if (e8m0)
+    hipLaunchKernelGGL((grouped_gemm_kernel<false, true>), dim3(grid), dim3(NTHR), 0, stream, s2, offsets);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<false, false>), dim3(grid), dim3(NTHR), 0, stream, s2, offsets);
   return hipGetLastError();
 }
 

@@ -54,7 +54,9 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* p) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <bool SWIGLU>
+// POW2: H is requantised with the power-of-two scale rule (the variant whose
+// scales are all powers of two; with such scales the promotion is exact).
+template <bool SWIGLU, bool POW2>
 __global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
     SmallArgs p, const int32_t* __restrict__ offsets) {
   __shared__ int smTile[SM_MAX_GROUPS + 1];        // m-chunk prefix over groups
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
         float a = sAmax[0][r];
 #pragma unroll
         for (int w = 1; w < SM_THREADS / 64; ++w) a = fmaxf(a, sAmax[w][r]);
-        const float sc = scale_from_amax(a);
+        const float sc = tile_scale<POW2>(a);
         if (r < rows_valid) {
           const float rs = __builtin_amdgcn_rcpf(sc);
           const float r1 = fmaf(fmaf(-sc, rs, 1.0f), rs, rs);   // reciprocal, one Newton step
@@ -254,13 +256,19 @@ static int num_cus_small() {
 hipError_t launch_gemm_up_small(const uint8_t* aq, const float* as, int a_rows,
                                 const int32_t* row_src, const int32_t* offsets, int n_groups,
                                 int total_rows, int d, int f, const uint8_t* w13,
-                                const float* w13_s, uint8_t* h, float* hs, hipStream_t stream) {
+                                const float* w13_s, uint8_t* h, float* hs, bool pow2,
+                                hipStream_t stream) {
   SmallArgs s{};
   s.a = aq; s.as = as; s.a_rows = a_rows; s.row_src = row_src; s.n_groups = n_groups;
   s.total_rows = total_rows; s.K = d; s.N = 2 * f; s.n_tiles_n = f / 128; s.b = w13; s.bs = w13_s;
   s.f = f; s.h = h; s.hs = hs;
   const int grid = ((num_cus_small() + 7) / 8) * 8;   // persistent: one workgroup per CU
-  hipLaunchKernelGGL(grouped_gemm_small_kernel<true>, dim3(grid), dim3(SM_THREADS), 0, stream, s, offsets);
+  if (pow2)
+    hipLaunchKernelGGL((grouped_gemm_small_kernel<true, true>), dim3(grid), dim3(SM_THREADS), 0, stream, s,
+                       offsets);
+  else
+    hipLaunchKernelGGL((grouped_gemm_small_kernel<true, false>), dim3(grid), dim3(SM_THREADS), 0, stream, s,
+                       offsets);
   return hipGetLastError();
 }
 
@@ -272,7 +280,8 @@ hipError_t launch_gemm_down_small(const uint8_t* h, const float* hs, const int32
   s.total_rows = total_rows; s.K = f; s.N = d; s.n_tiles_n = (d + 255) / 256; s.b = w2; s.bs = w2_s;
   s.f = f; s.y = y;
   const int grid = ((num_cus_small() + 7) / 8) * 8;   // persistent: one workgroup per CU
-  hipLaunchKernelGGL(grouped_gemm_small_kernel<false>, dim3(grid), dim3(SM_THREADS), 0, stream, s, offsets);
+  hipLaunchKernelGGL((grouped_gemm_small_kernel<false, false>), dim3(grid), dim3(SM_THREADS), 0, stream, s,
+                     offsets);
   return hipGetLastError();
 }
 

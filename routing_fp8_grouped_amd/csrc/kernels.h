@@ -10,9 +10,9 @@
 namespace moe {
 
 hipError_t launch_quant_1x128(const uint16_t* x, long rows, int cols, uint8_t* q, float* scale,
-                              hipStream_t stream);
+                              bool pow2, hipStream_t stream);
 hipError_t launch_quant_128x128(const uint16_t* w, int N, int K, uint8_t* q, float* scale,
-                                hipStream_t stream);
+                                bool pow2, hipStream_t stream);
 
 hipError_t launch_route(const uint16_t* x, const uint16_t* wg, const float* bias, int T, int d,
                         int E, int G, int M, int k, float route_scale, int32_t* idx, float* w,
@@ -27,17 +27,18 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const uint8_t
 hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const int32_t* row_src,
                           const int32_t* offsets, int n_groups, int total_rows, int d, int f,
                           const uint8_t* w13, const float* w13_s, uint8_t* h, float* hs,
-                          hipStream_t stream);
+                          bool e8m0, hipStream_t stream);
 hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* offsets, int n_groups,
                             int total_rows, int d, int f, const uint8_t* w2, const float* w2_s,
-                            uint16_t* y, hipStream_t stream);
+                            uint16_t* y, bool e8m0, hipStream_t stream);
 
 // Variants of the two expert GEMMs for few rows per group (weight streaming;
 // launch_gemm_up/down choose them when total_rows <= 16 * n_groups).
 hipError_t launch_gemm_up_small(const uint8_t* aq, const float* as, int a_rows,
                                 const int32_t* row_src, const int32_t* offsets, int n_groups,
                                 int total_rows, int d, int f, const uint8_t* w13,
-                                const float* w13_s, uint8_t* h, float* hs, hipStream_t stream);
+                                const float* w13_s, uint8_t* h, float* hs, bool pow2,
+                                hipStream_t stream);
 hipError_t launch_gemm_down_small(const uint8_t* h, const float* hs, const int32_t* offsets,
                                   int n_groups, int total_rows, int d, int f, const uint8_t* w2,
                                   const float* w2_s, uint16_t* y, hipStream_t stream);

@@ -10,7 +10,9 @@ namespace moe {
 
 // One 1x128 tile per 16 lanes; each lane owns 8 consecutive elements (one
 // 16-byte load, one 8-byte store).  The amax reduction stays inside the 16-lane
-// group (xor shuffles with masks < 16).
+// group (xor shuffles with masks < 16).  POW2 selects the power-of-two scale
+// rule (smallest power of two not below amax/448).
+template <bool POW2>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __restrict__ x,
                                                           long n_tiles,
                                                           uint8_t* __restrict__ q,
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  const float s = scale_from_amax(amax);
+  const float s = tile_scale<POW2>(amax);
   uint2 out;
   out.x = f32x4_to_e4m3(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
   out.y = f32x4_to_e4m3(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
@@ -44,6 +46,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
 
 // One 128x128 block per workgroup: thread t owns 64 elements of row t/2
 // (columns (t%2)*64 .. +64).  Block amax through wave shuffles and LDS.
+template <bool POW2>
 __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ w,
                                                             int K,
                                                             uint8_t* __restrict__ q,
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __re
   if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
-  const float s = scale_from_amax(amax);
+  const float s = tile_scale<POW2>(amax);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     uint4 out;
@@ -84,18 +87,26 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __re
 }
 
 hipError_t launch_quant_1x128(const uint16_t* x, long rows, int cols, uint8_t* q, float* scale,
-                              hipStream_t stream) {
+                              bool pow2, hipStream_t stream) {
   const long n_tiles = rows * (long)(cols / 128);
   const long blocks = (n_tiles + 15) / 16;
-  hipLaunchKernelGGL(quant_1x128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n_tiles, q,
-                     scale);
+  if (pow2)
+    hipLaunchKernelGGL(quant_1x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       n_tiles, q, scale);
+  else
+    hipLaunchKernelGGL(quant_1x128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       n_tiles, q, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_128x128(const uint16_t* w, int N, int K, uint8_t* q, float* scale,
-                                hipStream_t stream) {
-  hipLaunchKernelGGL(quant_128x128_kernel, dim3(K / 128, N / 128), dim3(256), 0, stream, w, K, q,
-                     scale);
+                                bool pow2, hipStream_t stream) {
+  if (pow2)
+    hipLaunchKernelGGL(quant_128x128_kernel<true>, dim3(K / 128, N / 128), dim3(256), 0, stream, w,
+                       K, q, scale);
+  else
+    hipLaunchKernelGGL(quant_128x128_kernel<false>, dim3(K / 128, N / 128), dim3(256), 0, stream, w,
+                       K, q, scale);
   return hipGetLastError();
 }
 

@@ -37,13 +37,14 @@ def rel_l2_rows(a, b):
     return num / np.maximum(den, 1e-30)
 
 
-def device_weights(cfg, bf16_cache=None):
+def device_weights(cfg, bf16_cache=None, pow2=False):
     """Generate every expert's BF16 weights on the GPU (seeded per expert) and
-    quantise them with the library's 128x128 kernel (the offline step)."""
+    quantise them with the library's 128x128 kernel (the offline step; the
+    power-of-two scale rule when ``pow2``)."""
     W = moe.MoEWeights.empty(cfg.E + 1, cfg.d, cfg.f)
     for e in range(cfg.E + 1):
         w13, w2 = inputs.expert_weights(cfg, e, DEV)
-        W.quantize_expert(e, w13, w2)
+        W.quantize_expert(e, w13, w2, pow2=pow2)
         if bf16_cache is not None:
             bf16_cache[e] = (w13, w2)
     torch.cuda.synchronize()
@@ -55,10 +56,11 @@ class OracleExperts:
     oracle from the same BF16 weights the GPU quantised (regenerated per expert
     with the same seed, copied to the host)."""
 
-    def __init__(self, cfg, bf16_cache=None):
+    def __init__(self, cfg, bf16_cache=None, rule="fp32"):
         self.cfg = cfg
         self.cache = {}
         self.bf16 = bf16_cache
+        self.rule = rule
 
     def _host(self, e):
         if self.bf16 is not None and e in self.bf16:
@@ -74,7 +76,7 @@ class OracleExperts:
         host = {e: self._host(e) for e in ids}
         workers = workers or min(16, os.cpu_count() or 4)
         with cf.ThreadPoolExecutor(workers) as ex:
-            res = ex.map(lambda e: (e, olayer.quantize_expert(*host[e])), ids)
+            res = ex.map(lambda e: (e, olayer.quantize_expert(*host[e], self.rule)), ids)
             for e, q in res:
                 self.cache[e] = q
 
@@ -89,9 +91,9 @@ def host_inputs(cfg):
     return x, wg, b
 
 
-def run_layer(cfg, x, wg, b, W, dispatch=False):
+def run_layer(cfg, x, wg, b, W, dispatch=False, scales="fp32"):
     L = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.f, cfg.route_scale,
-                     dispatch=dispatch)
+                     dispatch=dispatch, scales=scales)
     L.forward(x.to(DEV), wg.to(DEV), b.to(DEV), W)
     torch.cuda.synchronize()
     return L
@@ -132,13 +134,24 @@ def block_abs_sums(aq_rows, as_rows, wq, ws):
     return np.sqrt(ss), mx
 
 
+# Over 56 K blocks (K = 7168) on E4M3 codes of Gaussian data, measured on
+# gfx950 over 131,072 outputs: |error| has RMS 1.07 sigma (sigma = the RMS above
+# times the root-sum-square of the blocks' s*sum|a*b|), maximum 6.58 sigma and
+# 1.92 times the single-block bound; chaining the accumulator through the
+# block-scaled instruction gives the same errors as promoting each partial in
+# FP32.  The band takes 8 sigma and 3 times the single-block bound, for a
+# margin over the tails of the ~10^6 outputs of a test.
+NOISE_SIGMAS = 8.0
+NOISE_BLOCKS = 3.0
+
+
 def gemm_noise(aq_rows, as_rows, wq, ws, acc):
-    """Bound on |GPU - exact| of a blocked GEMM output: 6 RMS of the
-    independent block errors, at least twice the worst single-block error,
-    plus FP32 accumulation."""
+    """Bound on |GPU - exact| of a blocked GEMM output: NOISE_SIGMAS RMS of the
+    independent block errors, at least NOISE_BLOCKS times the worst
+    single-block error, plus FP32 accumulation."""
     root, mx = block_abs_sums(aq_rows, as_rows, wq, ws)
     kb = np.asarray(aq_rows).shape[1] // 128
-    return (np.maximum(6 * MFMA_BLOCK_RMS * root, 2 * MFMA_BLOCK_MAX * mx)
+    return (np.maximum(NOISE_SIGMAS * MFMA_BLOCK_RMS * root, NOISE_BLOCKS * MFMA_BLOCK_MAX * mx)
             + kb * 2.0 ** -24 * np.abs(acc))
 
 
@@ -149,13 +162,8 @@ def e4m3_spacing(v):
     return np.ldexp(1.0, np.maximum(p - 1, -6) - 3)
 
 
-def h_code_ambiguity(aq_rows, as_rows, w13q, w13s, g, u, h, hs):
-    """(amb, step) for the rows' h codes: amb marks elements whose scaled value
-    lies within the noise band of a rounding midpoint; step bounds how far
-    (in scaled units) a valid code of such an element can be from the oracle's:
-    the GPU code rounds some value inside the band, so the two codes differ by
-    at most twice the band plus one grid spacing (near zero the band can cover
-    several subnormal steps)."""
+def h_noise(aq_rows, as_rows, w13q, w13s, g, u, h):
+    """Bound on |GPU h - oracle h| per element, from oracle quantities."""
     f = w13q.shape[0] // 2
     g = np.asarray(g, np.float64); u = np.asarray(u, np.float64); h = np.asarray(h, np.float64)
     e = gemm_noise(aq_rows, as_rows, w13q, w13s, np.concatenate([g, u], axis=1))
@@ -164,7 +172,33 @@ def h_code_ambiguity(aq_rows, as_rows, w13q, w13s, g, u, h, hs):
     dsilu = sig * (1.0 + g * (1.0 - sig))
     # FP32 SwiGLU: the kernel's SiLU (exp within an ulp, hardware reciprocal)
     # and the product with u sit a few ulp from the exactly rounded value
-    eh = np.abs(u) * np.abs(dsilu) * eg + np.abs(g * sig) * eu + 2.0 ** -20 * np.abs(h)
+    return np.abs(u) * np.abs(dsilu) * eg + np.abs(g * sig) * eu + 2.0 ** -20 * np.abs(h)
+
+
+def pow2_scale_choices(h, eh):
+    """Per 1x128 tile of h: the power-of-two scales the GPU may legitimately
+    pick (lowest, highest).  They differ where amax/448 lies within the noise
+    of amax from a power of two; then either choice is correct."""
+    rows = h.shape[0]
+    ht = np.abs(np.asarray(h, np.float64)).reshape(rows, -1, 128)
+    et = np.asarray(eh, np.float64).reshape(rows, -1, 128)
+    lo = np.max(np.maximum(ht - et, 0.0), -1).astype(np.float32)
+    hi = np.max(ht + et, -1).astype(np.float32)
+    return oquant.scale_from_amax(lo, "pow2"), oquant.scale_from_amax(hi, "pow2")
+
+
+def h_code_ambiguity(aq_rows, as_rows, w13q, w13s, g, u, h, hs, rule="fp32"):
+    """(amb, step) for the rows' h codes: amb marks elements whose scaled value
+    lies within the noise band of a rounding midpoint; step bounds how far
+    (in scaled units) a valid code of such an element can be from the oracle's:
+    the GPU code rounds some value inside the band, so the two codes differ by
+    at most twice the band plus one grid spacing (near zero the band can cover
+    several subnormal steps).  With the power-of-two rule a tile whose scale
+    may legitimately be the next power up or down is ambiguous as a whole: its
+    GPU values sit on a grid up to twice as coarse, i.e. within twice the
+    band plus three spacings of the oracle's (in the oracle's scaled units)."""
+    g = np.asarray(g, np.float64); u = np.asarray(u, np.float64); h = np.asarray(h, np.float64)
+    eh = h_noise(aq_rows, as_rows, w13q, w13s, g, u, h)
     rows = h.shape[0]
     ht = np.abs(h).reshape(rows, -1, 128)
     et = eh.reshape(rows, -1, 128)
@@ -179,14 +213,33 @@ def h_code_ambiguity(aq_rows, as_rows, w13q, w13s, g, u, h, hs):
     sp_below = e4m3_spacing(np.maximum(lo - sp / 4, 0.0))
     dist = np.minimum(np.abs(y - (lo + sp / 2)), np.abs(y - (lo - sp_below / 2)))
     step = 2.0 * band + e4m3_spacing(y + band)
-    return dist <= band, step
+    amb = dist <= band
+    h_code_ambiguity.margin = dist / np.maximum(band, 1e-300)   # for failure reports
+    h_code_ambiguity.y = y
+    if rule == "pow2":
+        s_lo, s_hi = pow2_scale_choices(h, eh)
+        flip = np.repeat(s_lo != s_hi, 128, axis=1)
+        amb = amb | flip
+        step = np.where(flip, 2.0 * band + 3.0 * e4m3_spacing(2.0 * (y + band)), step)
+    return amb, step
 
 
 def check_h_codes(gh, hq, amb, step):
-    """Unambiguous codes equal; ambiguous ones within their allowed step."""
+    """Unambiguous codes equal; ambiguous ones within their allowed step.  The
+    two zero codes (+0, -0) count as equal: a value that rounds to zero has the
+    sign of an h that is itself within noise of zero."""
     from oracle import fp8 as ofp8
-    same = gh == hq
-    assert np.all(same | amb), int(np.sum(~same & ~amb))
+    same = (gh == hq) | (((gh & 0x7F) == 0) & ((hq & 0x7F) == 0))
+    bad = ~same & ~amb
+    if np.any(bad):
+        m = getattr(h_code_ambiguity, "margin", None)
+        if m is not None and m.shape == bad.shape:
+            yv = h_code_ambiguity.y
+            print("  codes outside the band: distance to midpoint / band =",
+                  np.array2string(m[bad][:10], precision=3), "scaled value",
+                  np.array2string(yv[bad][:10], precision=4), "gpu", gh[bad][:10], "oracle", hq[bad][:10],
+                  flush=True)
+    assert np.all(same | amb), int(np.sum(bad))
     dv = np.abs(ofp8.e4m3_decode(gh) - ofp8.e4m3_decode(hq))
     assert np.all(dv[~same] <= 1.001 * step[~same])
     return int(np.sum(~same))
@@ -211,7 +264,7 @@ def rows_within(got, ref, allow, tol):
     return ok, err / nref, int(np.sum(err > tol * nref))
 
 
-def layer_allowance(res, experts, T, k, E):
+def layer_allowance(res, experts, T, k, E, rule="fp32"):
     """Bound on |delta out| [T, d] of a whole-batch oracle result (moe_layer)
     from the ambiguous h codes of every expert row, combined with the gates."""
     rows, d = res["y"].shape
@@ -226,7 +279,7 @@ def layer_allowance(res, experts, T, k, E):
         w13q, w13s, w2q, w2s = experts(e)
         amb, sp = h_code_ambiguity(res["xq_perm"][lo:hi], res["xs_perm"][lo:hi], w13q, w13s,
                                    res["g"][lo:hi], res["u"][lo:hi], res["h"][lo:hi],
-                                   res["hs"][lo:hi])
+                                   res["hs"][lo:hi], rule)
         amb_all[lo:hi], sp_all[lo:hi] = amb, sp
         allow[lo:hi] = y_allowance(amb, sp, res["hs"][lo:hi], w2q, w2s)
     w = np.asarray(res["route"]["w"], np.float64)
@@ -235,7 +288,7 @@ def layer_allowance(res, experts, T, k, E):
     return out_allow, amb_all, sp_all
 
 
-def token_allowance(extra, r, experts, E):
+def token_allowance(extra, r, experts, E, rule="fp32"):
     """The same bound for tokens evaluated on their own (moe_layer_tokens)."""
     n, k = r["idx"].shape
     d = extra["y_shared"].shape[1]
@@ -246,6 +299,6 @@ def token_allowance(extra, r, experts, E):
         for e, it, wt in slots:
             w13q, w13s, w2q, w2s = experts(int(e))
             amb, sp = h_code_ambiguity(extra["xq"][t:t + 1], extra["xs"][t:t + 1], w13q, w13s,
-                                       it["g"], it["u"], it["h"], it["hs"])
+                                       it["g"], it["u"], it["h"], it["hs"], rule)
             out[t] += wt * y_allowance(amb, sp, it["hs"], w2q, w2s)[0]
     return out

@@ -29,6 +29,8 @@ def test_exports_every_declared_symbol(lib):
                              "moe_permute_workspace_bytes", "moe_permute",
                              "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up",
                              "grouped_gemm_fp8_down", "moe_combine", "moe_bias_update",
+                             "fp8_quant_1x128_pow2", "fp8_quant_128x128_pow2",
+                             "grouped_gemm_fp8_up_e8m0", "grouped_gemm_fp8_down_e8m0",
                              "moe_status_string", "moe_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -85,6 +87,11 @@ def test_quant_validation(lib):
     assert lib.fp8_quant_128x128(A, 128, 0, A, A, None) == 1
     assert lib.fp8_quant_128x128(A, 128 * 70000, 128, A, A, None) == 2
     assert lib.fp8_quant_128x128(None, 0, 128, None, None, None) == 0
+    # the power-of-two variants validate the same way and name themselves
+    assert lib.fp8_quant_1x128_pow2(A, 4, 100, A, A, None) == 1 and "cols=100" in last(lib)
+    assert lib.fp8_quant_1x128_pow2(None, 0, 128, None, None, None) == 0
+    assert lib.fp8_quant_128x128_pow2(A, 100, 128, A, A, None) == 1 and "N=100" in last(lib)
+    assert lib.fp8_quant_128x128_pow2(A, 128 * 70000, 128, A, A, None) == 2
 
 
 def test_permute_validation_and_workspace(lib):
@@ -125,6 +132,14 @@ def test_gemm_validation(lib):
         A, A, A, 257, rows, 256, f, A, A, y, None)
     assert down(f=100) == 1 and down(y=MIS) == 1 and "y is not 16" in last(lib)
     assert down(rows=0, y=None) == 0
+    up8 = lambda rows=100, d=256, h=A, row_src=A: lib.grouped_gemm_fp8_up_e8m0(
+        A, A, 10, row_src, A, 257, rows, d, 128, A, A, h, A, None)
+    assert up8(d=100) == 1 and up8(h=None) == 1 and up8(row_src=None) == 1
+    assert up8(rows=0, h=None) == 0
+    down8 = lambda rows=100, f=128, y=A: lib.grouped_gemm_fp8_down_e8m0(
+        A, A, A, 257, rows, 256, f, A, A, y, None)
+    assert down8(f=100) == 1 and down8(y=MIS) == 1 and "y is not 16" in last(lib)
+    assert lib.grouped_gemm_fp8_up_e8m0(A, A, 10, A, A, 2000, 100, 256, 128, A, A, A, A, None) == 2
 
 
 def test_combine_validation(lib):

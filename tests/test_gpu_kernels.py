@@ -217,6 +217,7 @@ def gemm_case(rng, counts, d, f, a_rows, gather):
     ([0, 1, 130, 128, 257, 0], 256, 128, True),
     ([3, 0, 200, 64], 384, 256, True),
     ([129, 5], 512, 384, False),
+    ([300, 520, 17], 7168, 2048, True),     # the V3 shape on the tiled kernel
     # at most 16 rows per group on average: the weight-streaming kernels
     # (chunks of 16 rows, a partial 256-row block of W2 at d = 384)
     ([2, 1, 3], 7168, 2048, True),
