@@ -14,6 +14,9 @@ load, the headline case for the grouped FP8 GEMM.  ``roofline`` reports the
 dominant kernel (the first expert GEMM, 2/3 of the FLOPs) against the MI355X
 dense FP8 MFMA peak, timed with HIP events on the stream it runs on;
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+``e8m0_variant`` times the same workload once more with power-of-two scales on
+the hardware block-scaled MFMA (weights requantised with that rule, outside
+the timed region); the headline ``value`` is the FP32-scale method.
 """
 
 import argparse
@@ -61,11 +64,11 @@ def read_traffic(workload):
         return None
 
 
-def build_weights(cfg):
+def build_weights(cfg, pow2=False):
     W = moe.MoEWeights.empty(cfg.E + 1, cfg.d, cfg.f)
     for e in range(cfg.E + 1):
         w13, w2 = inputs.expert_weights(cfg, e, "cuda")
-        W.quantize_expert(e, w13, w2)
+        W.quantize_expert(e, w13, w2, pow2=pow2)
         del w13, w2
     torch.cuda.synchronize()
     return W
@@ -107,6 +110,27 @@ def cpu_baseline(cfg, n_tokens):
                       "quantised by the oracle beforehand (untimed, as on the GPU)"}
 
 
+def timed_steps(layer, x, wg, b, W, steps):
+    """Wall time per step over ``steps`` layer steps (bracketed by device
+    synchronisations) and per-stage times from HIP events recorded on the
+    stream the kernels run on."""
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        marks = ev[s]
+        marks[0].record(stream)
+        it = iter(marks[1:])
+        layer.forward(x, wg, b, W, mark=lambda name: next(it).record(stream))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+                for i, name in enumerate(STAGES)}
+    return (t1 - t0) * 1e3 / steps, stage_ms
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +141,8 @@ def main():
                     help="copy the FP8 rows into grouped order instead of gathering in the GEMM")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-e8m0", action="store_true",
+                    help="skip the timing of the power-of-two (E8M0) scale variant")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -150,21 +176,7 @@ def main():
     torch.cuda.synchronize()
     log(f"{args.warmup} warmup steps done")
 
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        marks = ev[s]
-        marks[0].record(stream)
-        it = iter(marks[1:])
-        layer.forward(x, wg, b, W, mark=lambda name: next(it).record(stream))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
-                for i, name in enumerate(STAGES)}
+    ms_per_step, stage_ms = timed_steps(layer, x, wg, b, W, args.steps)
     log(f"{args.steps} timed steps: {ms_per_step:.3f} ms/step; stages " +
         ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
 
@@ -208,7 +220,7 @@ def main():
                    "groups_per_token": cfg.M, "topk": cfg.k, "d_ffn": cfg.f,
                    "route_scale": cfg.route_scale, "dispatch_copy": args.dispatch},
         "roofline": dict(roof, traffic=traffic,
-                         kernel="grouped_gemm_fp8_up (grouped_gemm_kernel<true>)",
+                         kernel="grouped_gemm_fp8_up (grouped_gemm_kernel<true, false>)",
                          flop_per_launch=up_flop, algorithmic_bytes_per_launch=up_bytes,
                          avg_launch_ms=stage_ms["gemm_up"], tflops=up_tflops),
         "stages_ms": stage_ms,
@@ -220,6 +232,25 @@ def main():
         "context": "pages: 2.788M H800 GPU-hours for the whole V3 training run; "
                    "180K H800 GPU-hours per trillion training tokens (not comparable)",
     }
+    if not args.no_e8m0:
+        del W, layer
+        torch.cuda.empty_cache()
+        W8 = build_weights(cfg, pow2=True)
+        layer8 = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.f, cfg.route_scale,
+                              dispatch=args.dispatch, scales="pow2")
+        for _ in range(args.warmup):
+            layer8.forward(x, wg, b, W8)
+        ms8, st8 = timed_steps(layer8, x, wg, b, W8, args.steps)
+        log(f"E8M0 variant: {ms8:.3f} ms/step; stages " + ", ".join(f"{k} {v:.3f}" for k, v in st8.items()))
+        up8 = up_flop / (st8["gemm_up"] * 1e-3) / 1e12
+        result["e8m0_variant"] = {
+            "scales": "power of two, hardware block-scaled MFMA",
+            "value": cfg.T / (ms8 * 1e-3), "unit": "tokens/s", "ms_per_step": ms8,
+            "stages_ms": st8, "gemm_up_tflops": up8, "gemm_up_frac_of_fp8_peak": up8 / FP8_PEAK_TFLOPS,
+            "grouped_gemm_tflops": (up_flop + down_flop) / ((st8["gemm_up"] + st8["gemm_down"]) * 1e-3) / 1e12,
+            "kernel": "grouped_gemm_fp8_up_e8m0 (grouped_gemm_kernel<true, true>)",
+        }
+        del W8, layer8
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_tokens} token(s)")
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)

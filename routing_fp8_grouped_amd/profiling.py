@@ -30,16 +30,24 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 GEMM_SOURCES = ["routing_fp8_grouped_amd/csrc/gemm.hip", "routing_fp8_grouped_amd/csrc/common.h"]
 KERNELS = {
-    "grouped_gemm_kernel<true>": "grouped_gemm_fp8_up",
-    "grouped_gemm_kernel<false>": "grouped_gemm_fp8_down",
+    "grouped_gemm_kernel<true, false>": "grouped_gemm_fp8_up",
+    "grouped_gemm_kernel<false, false>": "grouped_gemm_fp8_down",
+    "grouped_gemm_kernel<true, true>": "grouped_gemm_fp8_up_e8m0",
+    "grouped_gemm_kernel<false, true>": "grouped_gemm_fp8_down_e8m0",
+    "grouped_gemm_small_kernel<true, false>": "grouped_gemm_fp8_up (few rows)",
+    "grouped_gemm_small_kernel<true, true>": "grouped_gemm_fp8_up_e8m0 (few rows)",
+    "grouped_gemm_small_kernel<false, false>": "grouped_gemm_fp8_down (few rows)",
     "route_kernel": "moe_route",
-    "quant_1x128_kernel": "fp8_quant_1x128",
-    "quant_128x128_kernel": "fp8_quant_128x128",
+    "quant_1x128_kernel<false>": "fp8_quant_1x128",
+    "quant_128x128_kernel<false>": "fp8_quant_128x128",
+    "quant_1x128_kernel<true>": "fp8_quant_1x128_pow2",
+    "quant_128x128_kernel<true>": "fp8_quant_128x128_pow2",
     "permute_count": "moe_permute (count)",
     "permute_scan": "moe_permute (scan)",
     "permute_scatter": "moe_permute (scatter)",
     "permute_gather": "moe_permute (gather)",
     "combine_kernel": "moe_combine",
+    "bias_update_kernel": "moe_bias_update",
 }
 GIB_KIB = float(1 << 20)
 
@@ -99,7 +107,7 @@ def per_dispatch(d, counter):
     return {k: (names[k], v) for k, v in vals.items()}
 
 
-def traffic(fetch_dir, write_dir, kernel_frag="grouped_gemm_kernel<true>"):
+def traffic(fetch_dir, write_dir, kernel_frag="grouped_gemm_kernel<true, false>"):
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         disp = per_dispatch(d, counter)
