@@ -229,6 +229,108 @@ moe_status grouped_gemm_fp8_down_e8m0(const uint8_t* h, const float* hs, const i
                                       const uint8_t* w2, const float* w2_s,
                                       uint16_t* y, void* stream);
 
+/* ---- Backward of the layer (training) ----
+ * The pages run all three GEMMs of each linear layer in FP8 (summary page
+ * section 6: Fprop, Dgrad, Wgrad), cache the SwiGLU inputs in FP8 and
+ * recompute SwiGLU in the backward, and regroup 1x128 tiles into 128x1 tiles
+ * with power-of-two scales where a backward GEMM needs the other orientation
+ * (book chapter 17; chapter 16 "Why transposition is not trivial").  Every
+ * quantisation below uses the power-of-two rule of the E8M0 section above.
+ *
+ * Dgrad needs no entry point of its own: grouped_gemm_fp8_down computes
+ * y = A * B^T for any (N, K) = (d, f) and, given the transposed weights
+ * (moe_transpose_fp8_blocks), gives dH = dY * W2 (A = dY, B = W2^T [E+1, f, d])
+ * and the expert-input gradient [dG, dU] * W13 (B = W13^T [E+1, d, 2f]).  The
+ * token gradient is moe_combine with all weights 1.
+ *
+ * Wgrad operands are "K-major": a [C, Kp] byte matrix whose row c holds column
+ * c of the operand for every row of every expert, expert e in the column range
+ * [128 pb[e], 128 pb[e+1]), pb[e] = sum over earlier experts of
+ * ceil(rows/128), padding columns zero codes; scales [Kp/128, C], one per
+ * column and 128-row block; Kp = moe_wgrad_columns(total_rows, n_groups)
+ * (columns past 128 pb[n_groups] are not written). */
+
+/* grouped_gemm_fp8_up_train — grouped_gemm_fp8_up (same arguments, rules and
+ * errors) that also writes the SwiGLU input the backward recomputes from
+ * (book chapter 17 "SwiGLU recomputation"): [G, U] quantised in 1x128 tiles
+ * with the forward's rule (amax/448):
+ *   gu [total_rows, 2f] E4M3 out (columns [0, f) = G, [f, 2f) = U),
+ *   gus [total_rows, 2f/128] FP32 out.
+ * Always runs the tiled kernel. */
+moe_status grouped_gemm_fp8_up_train(const uint8_t* aq, const float* as, int a_rows,
+                                     const int32_t* row_src, const int32_t* offsets,
+                                     int n_groups, int total_rows, int d, int f,
+                                     const uint8_t* w13, const float* w13_s,
+                                     uint8_t* h, float* hs, uint8_t* gu, float* gus, void* stream);
+
+/* moe_transpose_fp8_blocks — for each of n_matrices [N, K] E4M3 matrices with
+ * [N/128, K/128] block scales, the [K, N] transpose with [K/128, N/128] scales
+ * (exact: a block scale serves both orientations).  Offline, once per weight
+ * update.  w, wt device; wt must not alias w. */
+moe_status moe_transpose_fp8_blocks(const uint8_t* w, const float* ws, int n_matrices, int N, int K,
+                                    uint8_t* wt, float* wts, void* stream);
+
+/* moe_combine_backward — gradients of moe_combine (book chapter 7 "Selecting
+ * and combining experts"): for every token t and slot j,
+ *   dy[pos[t][j]]     = BF16(w[t][j] * dout[t])      (FP32 product)
+ *   dw[t][j]          = sum_c dout[t][c] * y[pos[t][j]][c]   (FP32 sum)
+ *   dy[shared_row0+t] = dout[t]   (when shared_row0 >= 0)
+ *   dout [T, d] BF16; y [rows, d] BF16 (the forward's expert outputs);
+ *   pos, w [T, k]; dy [rows, d] BF16 out; dw [T, k] FP32 out. */
+moe_status moe_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
+                                const float* w, int T, int k, int d, int32_t shared_row0,
+                                uint16_t* dy, float* dw, void* stream);
+
+/* moe_wgrad_columns — Kp of the K-major layout for total_rows rows in n_groups
+ * groups: 128 * (total_rows / 128 + n_groups), an upper bound of
+ * 128 pb[n_groups] that depends only on host-known sizes (0 on bad input). */
+int moe_wgrad_columns(int total_rows, int n_groups);
+
+/* moe_regroup_128x1 — the K-major 128x1 power-of-two FP8 copy (out [C, Kp],
+ * out_s [Kp/128, C]) of one operand of Wgrad, from either
+ *   xq, xs   a 1x128 FP8 tensor ([*, C] codes, [*, C/128] scales) whose row r
+ *            of the grouped order is row row_src[r] (row r when NULL): the
+ *            forward's cache of X, dequantised in FP32 and requantised; or
+ *   x_bf16   a BF16 tensor [total_rows, C] in grouped order (dY)
+ * (exactly one of xq and x_bf16).  offsets [n_groups + 1] as for the GEMMs.
+ * MOE_ERR_UNSUPPORTED: n_groups > 1024, more than 65535 padded row blocks, or
+ * C * Kp above 2^32 bytes. */
+moe_status moe_regroup_128x1(const uint8_t* xq, const float* xs, const uint16_t* x_bf16,
+                             const int32_t* row_src, const int32_t* offsets, int n_groups,
+                             int total_rows, int C, uint8_t* out, float* out_s, void* stream);
+
+/* moe_swiglu_backward — SwiGLU backward recomputed from the forward's FP8 cache
+ * (book chapter 17 "SwiGLU recomputation").  Per row r of the grouped order
+ * and column j < f, with g, u the cached [G, U] codes times their 1x128 scales
+ * (FP32) and s = sigmoid(g), evaluated in FP64 and rounded once to FP32:
+ *   h = g s u,  dG = dH u s (1 + g (1 - s)),  dU = dH g s
+ *   gu, gus    [rows, 2f] E4M3 and [rows, 2f/128] FP32: the cache ([G, U])
+ *   dh         [rows, f] BF16
+ *   dgu, dgus  [rows, 2f] / [rows, 2f/128] out: [dG, dU], 1x128 power-of-two
+ *              (the Dgrad operand)
+ *   dgu_t, dgu_ts  K-major [2f, Kp] / [Kp/128, 2f] out: [dG, dU] in 128x1 tiles
+ *   h_t, h_ts      K-major [f, Kp] / [Kp/128, f] out: h in 128x1 tiles
+ * (the Wgrad operands of W13 and W2). */
+moe_status moe_swiglu_backward(const uint8_t* gu, const float* gus, const uint16_t* dh,
+                               const int32_t* offsets, int n_groups, int total_rows, int f,
+                               uint8_t* dgu, float* dgus, uint8_t* dgu_t, float* dgu_ts,
+                               uint8_t* h_t, float* h_ts, void* stream);
+
+/* grouped_gemm_fp8_wgrad — weight gradients of all experts (summary page
+ * section 6, Wgrad in FP8): for every group e with rows [offsets[e],
+ * offsets[e+1]),
+ *   dw[e][m][n] = sum over the group's rows r of A(r, m) * B(r, n)
+ * where A and B are K-major 128x1 operands (moe_regroup_128x1,
+ * moe_swiglu_backward): a_t [M, Kp] / a_ts [Kp/128, M], b_t [N, Kp] /
+ * b_ts [Kp/128, N], Kp = moe_wgrad_columns(total_rows, n_groups), all scales
+ * powers of two (they go to the block-scaled MFMA as E8M0 codes).
+ *   dw [n_groups, M, N] FP32 out (zeros for a group without rows).
+ * dW2 = grouped_gemm_fp8_wgrad(dY_t, H_t) with (M, N) = (d, f); dW13 =
+ * grouped_gemm_fp8_wgrad([dG, dU]_t, X_t) with (M, N) = (2f, d). */
+moe_status grouped_gemm_fp8_wgrad(const uint8_t* a_t, const float* a_ts, const uint8_t* b_t,
+                                  const float* b_ts, const int32_t* offsets, int n_groups,
+                                  int total_rows, int M, int N, float* dw, void* stream);
+
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 

@@ -18,7 +18,9 @@ from ._lib import MoEError, RouteParams  # noqa: F401
 __all__ = ["moe_route", "fp8_quant_1x128", "fp8_quant_128x128", "moe_permute_workspace_bytes",
            "moe_permute", "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up", "grouped_gemm_fp8_down",
            "moe_combine", "moe_bias_update", "fp8_quant_1x128_pow2", "fp8_quant_128x128_pow2",
-           "grouped_gemm_fp8_up_e8m0", "grouped_gemm_fp8_down_e8m0", "MoEWeights", "MoELayer",
+           "grouped_gemm_fp8_up_e8m0", "grouped_gemm_fp8_down_e8m0", "grouped_gemm_fp8_up_train",
+           "moe_transpose_fp8_blocks", "moe_combine_backward", "moe_wgrad_columns", "moe_regroup_128x1",
+           "moe_swiglu_backward", "grouped_gemm_fp8_wgrad", "MoEWeights", "MoELayer",
            "MoEError", "RouteParams"]
 
 
@@ -195,6 +197,91 @@ def moe_bias_update(offsets, bias, gamma, stream=None):
                                                       _stream(stream)))
 
 
+def grouped_gemm_fp8_up_train(aq, as_, row_src, offsets, w13, w13_s, h, hs, gu, gus, stream=None):
+    """grouped_gemm_fp8_up that also writes the FP8 cache of [G, U] (gu [rows, 2f],
+    gus [rows, 2f/128]) for the backward's SwiGLU recomputation."""
+    for t, dt, n in ((aq, torch.uint8, "aq"), (as_, torch.float32, "as"),
+                     (row_src, torch.int32, "row_src"), (offsets, torch.int32, "offsets"),
+                     (w13, torch.uint8, "w13"), (w13_s, torch.float32, "w13_s"),
+                     (h, torch.uint8, "h"), (hs, torch.float32, "hs"), (gu, torch.uint8, "gu"),
+                     (gus, torch.float32, "gus")):
+        _dev(t, dt, n)
+    n_groups, two_f, d = w13.shape
+    lib = _lib.load()
+    _lib.check("grouped_gemm_fp8_up_train", lib.grouped_gemm_fp8_up_train(
+        _ptr(aq), _ptr(as_), aq.shape[0], _ptr(row_src), _ptr(offsets), n_groups, h.shape[0], d,
+        two_f // 2, _ptr(w13), _ptr(w13_s), _ptr(h), _ptr(hs), _ptr(gu), _ptr(gus), _stream(stream)))
+
+
+def moe_transpose_fp8_blocks(w, ws, wt, wts, stream=None):
+    """[G, N, K] E4M3 + [G, N/128, K/128] scales -> [G, K, N] + [G, K/128, N/128]."""
+    for t, dt, n in ((w, torch.uint8, "w"), (ws, torch.float32, "ws"), (wt, torch.uint8, "wt"),
+                     (wts, torch.float32, "wts")):
+        _dev(t, dt, n)
+    G, N, K = w.shape
+    lib = _lib.load()
+    _lib.check("moe_transpose_fp8_blocks", lib.moe_transpose_fp8_blocks(
+        _ptr(w), _ptr(ws), G, N, K, _ptr(wt), _ptr(wts), _stream(stream)))
+
+
+def moe_combine_backward(dout, y, pos, w, shared_row0, dy, dw, stream=None):
+    """dy [rows, d] BF16 and dw [T, k] FP32 from dout [T, d] and the forward's y."""
+    for t, dt, n in ((dout, torch.bfloat16, "dout"), (y, torch.bfloat16, "y"), (pos, torch.int32, "pos"),
+                     (w, torch.float32, "w"), (dy, torch.bfloat16, "dy"), (dw, torch.float32, "dw")):
+        _dev(t, dt, n)
+    T, k = pos.shape
+    lib = _lib.load()
+    _lib.check("moe_combine_backward", lib.moe_combine_backward(
+        _ptr(dout), _ptr(y), _ptr(pos), _ptr(w), T, k, dout.shape[1], shared_row0, _ptr(dy),
+        _ptr(dw), _stream(stream)))
+
+
+def moe_wgrad_columns(total_rows, n_groups):
+    return int(_lib.load().moe_wgrad_columns(total_rows, n_groups))
+
+
+def moe_regroup_128x1(offsets, n_groups, total_rows, out, out_s, xq=None, xs=None, x_bf16=None,
+                      row_src=None, stream=None):
+    """K-major 128x1 power-of-two copy out [C, Kp], out_s [Kp/128, C] of either
+    a 1x128 FP8 tensor (xq, xs, gathered through row_src) or a BF16 one."""
+    for t, dt, n in ((offsets, torch.int32, "offsets"), (out, torch.uint8, "out"),
+                     (out_s, torch.float32, "out_s"), (xq, torch.uint8, "xq"), (xs, torch.float32, "xs"),
+                     (x_bf16, torch.bfloat16, "x_bf16"), (row_src, torch.int32, "row_src")):
+        _dev(t, dt, n)
+    C = out.shape[0]
+    lib = _lib.load()
+    _lib.check("moe_regroup_128x1", lib.moe_regroup_128x1(
+        _ptr(xq), _ptr(xs), _ptr(x_bf16), _ptr(row_src), _ptr(offsets), n_groups, total_rows, C,
+        _ptr(out), _ptr(out_s), _stream(stream)))
+
+
+def moe_swiglu_backward(gu, gus, dh, offsets, n_groups, dgu, dgus, dgu_t, dgu_ts, h_t, h_ts, stream=None):
+    """SwiGLU backward from the FP8 [G, U] cache: the Dgrad operand (dgu, dgus)
+    and the K-major Wgrad operands of [dG, dU] and h."""
+    for t, dt, n in ((gu, torch.uint8, "gu"), (gus, torch.float32, "gus"), (dh, torch.bfloat16, "dh"),
+                     (offsets, torch.int32, "offsets"), (dgu, torch.uint8, "dgu"),
+                     (dgus, torch.float32, "dgus"), (dgu_t, torch.uint8, "dgu_t"),
+                     (dgu_ts, torch.float32, "dgu_ts"), (h_t, torch.uint8, "h_t"), (h_ts, torch.float32, "h_ts")):
+        _dev(t, dt, n)
+    rows, f = dh.shape
+    lib = _lib.load()
+    _lib.check("moe_swiglu_backward", lib.moe_swiglu_backward(
+        _ptr(gu), _ptr(gus), _ptr(dh), _ptr(offsets), n_groups, rows, f, _ptr(dgu), _ptr(dgus),
+        _ptr(dgu_t), _ptr(dgu_ts), _ptr(h_t), _ptr(h_ts), _stream(stream)))
+
+
+def grouped_gemm_fp8_wgrad(a_t, a_ts, b_t, b_ts, offsets, n_groups, total_rows, dw, stream=None):
+    """dw [n_groups, M, N] FP32 from the K-major operands a_t [M, Kp], b_t [N, Kp]."""
+    for t, dt, n in ((a_t, torch.uint8, "a_t"), (a_ts, torch.float32, "a_ts"), (b_t, torch.uint8, "b_t"),
+                     (b_ts, torch.float32, "b_ts"), (offsets, torch.int32, "offsets"),
+                     (dw, torch.float32, "dw")):
+        _dev(t, dt, n)
+    lib = _lib.load()
+    _lib.check("grouped_gemm_fp8_wgrad", lib.grouped_gemm_fp8_wgrad(
+        _ptr(a_t), _ptr(a_ts), _ptr(b_t), _ptr(b_ts), _ptr(offsets), n_groups, total_rows,
+        a_t.shape[0], b_t.shape[0], _ptr(dw), _stream(stream)))
+
+
 class MoEWeights:
     """FP8 expert weights of one layer: w13 [E+1, 2f, d], w2 [E+1, d, f] E4M3
     with 128x128 block scales; index E is the shared expert."""
@@ -217,6 +304,21 @@ class MoEWeights:
         q = fp8_quant_128x128_pow2 if pow2 else fp8_quant_128x128
         q(w13_bf16, self.w13q[e], self.w13s[e], stream)
         q(w2_bf16, self.w2q[e], self.w2s[e], stream)
+
+    def transposed(self, stream=None):
+        """The weights as Dgrad multiplies them: W13^T [G, d, 2f] and W2^T
+        [G, f, d] with transposed block scales (moe_transpose_fp8_blocks)."""
+        G, d, f = self.n_groups, self.d, self.f
+        dev = dict(device=self.w13q.device)
+        t = MoEWeights.__new__(MoEWeights)
+        t.w13q = torch.empty(G, d, 2 * f, dtype=torch.uint8, **dev)
+        t.w13s = torch.empty(G, d // 128, 2 * f // 128, dtype=torch.float32, **dev)
+        t.w2q = torch.empty(G, f, d, dtype=torch.uint8, **dev)
+        t.w2s = torch.empty(G, f // 128, d // 128, dtype=torch.float32, **dev)
+        moe_transpose_fp8_blocks(self.w13q, self.w13s, t.w13q, t.w13s, stream)
+        moe_transpose_fp8_blocks(self.w2q, self.w2s, t.w2q, t.w2s, stream)
+        t.n_groups, t.d, t.f = G, d, f
+        return t
 
 
 class MoELayer:
@@ -256,9 +358,11 @@ class MoELayer:
         self.y = torch.empty(rows, d, dtype=torch.bfloat16, **dev)
         self.out = torch.empty(T, d, dtype=torch.bfloat16, **dev)
 
-    def forward(self, x, wg, bias, weights, stream=None, mark=None):
+    def forward(self, x, wg, bias, weights, stream=None, mark=None, train=False):
         """Run the layer on x [T, d].  ``mark(name)``, if given, is called after
-        each stage is enqueued (the bench records HIP events there)."""
+        each stage is enqueued (the bench records HIP events there).  With
+        ``train`` the first expert GEMM also caches [G, U] in FP8 for
+        ``backward`` (FP32-scale method only)."""
         mark = mark or (lambda name: None)
         moe_route(x, wg, bias, self.n_groups, self.topk_groups, self.k, self.route_scale,
                   self.idx, self.w, stream)
@@ -276,13 +380,84 @@ class MoELayer:
         mark("permute")
         up = grouped_gemm_fp8_up_e8m0 if self.pow2 else grouped_gemm_fp8_up
         down = grouped_gemm_fp8_down_e8m0 if self.pow2 else grouped_gemm_fp8_down
-        up(aq, as_, src, self.offsets, weights.w13q, weights.w13s, self.h, self.hs, stream)
+        if train:
+            if self.pow2:
+                raise ValueError("the training forward runs the FP32-scale method")
+            self._train_buffers()
+            grouped_gemm_fp8_up_train(aq, as_, src, self.offsets, weights.w13q, weights.w13s, self.h,
+                                      self.hs, self.gu, self.gus, stream)
+        else:
+            up(aq, as_, src, self.offsets, weights.w13q, weights.w13s, self.h, self.hs, stream)
         mark("gemm_up")
         down(self.h, self.hs, self.offsets, weights.w2q, weights.w2s, self.y, stream)
         mark("gemm_down")
         moe_combine(self.y, self.pos, self.w, self.T * self.k, self.out, stream)
         mark("combine")
         return self.out
+
+    def _train_buffers(self):
+        if getattr(self, "gu", None) is not None:
+            return
+        T, k, d, f, E = self.T, self.k, self.d, self.f, self.E
+        rows, G = T * k + T, E + 1
+        dev = dict(device=self.h.device)
+        kp = moe_wgrad_columns(rows, G)
+        self.gu = torch.empty(rows, 2 * f, dtype=torch.uint8, **dev)
+        self.gus = torch.empty(rows, 2 * f // 128, dtype=torch.float32, **dev)
+        self.dy = torch.empty(rows, d, dtype=torch.bfloat16, **dev)
+        self.dw = torch.empty(T, k, dtype=torch.float32, **dev)
+        self.dyq = torch.empty(rows, d, dtype=torch.uint8, **dev)
+        self.dys = torch.empty(rows, d // 128, dtype=torch.float32, **dev)
+        self.dh = torch.empty(rows, f, dtype=torch.bfloat16, **dev)
+        self.dgu = torch.empty(rows, 2 * f, dtype=torch.uint8, **dev)
+        self.dgus = torch.empty(rows, 2 * f // 128, dtype=torch.float32, **dev)
+        self.dgu_t = torch.empty(2 * f, kp, dtype=torch.uint8, **dev)
+        self.dgu_ts = torch.empty(kp // 128, 2 * f, dtype=torch.float32, **dev)
+        self.h_t = torch.empty(f, kp, dtype=torch.uint8, **dev)
+        self.h_ts = torch.empty(kp // 128, f, dtype=torch.float32, **dev)
+        self.dy_t = torch.empty(d, kp, dtype=torch.uint8, **dev)
+        self.dy_ts = torch.empty(kp // 128, d, dtype=torch.float32, **dev)
+        self.x_t = torch.empty(d, kp, dtype=torch.uint8, **dev)
+        self.x_ts = torch.empty(kp // 128, d, dtype=torch.float32, **dev)
+        self.dx_rows = torch.empty(rows, d, dtype=torch.bfloat16, **dev)
+        self.dx = torch.empty(T, d, dtype=torch.bfloat16, **dev)
+        self.ones = torch.ones(T, k, dtype=torch.float32, **dev)
+        self.dw13 = torch.empty(G, 2 * f, d, dtype=torch.float32, **dev)
+        self.dw2 = torch.empty(G, d, f, dtype=torch.float32, **dev)
+
+    def backward(self, dout, weights_t, stream=None, mark=None):
+        """Backward of the last ``forward(..., train=True)`` for the output
+        gradient dout [T, d] BF16, with ``weights_t = weights.transposed()``.
+        Returns (dX [T, d] BF16, dW13 [E+1, 2f, d] FP32, dW2 [E+1, d, f] FP32,
+        gate gradients [T, k] FP32).  Every backward quantisation uses
+        power-of-two scales; Dgrad runs on grouped_gemm_fp8_down with the
+        transposed weights, Wgrad on the K-major 128x1 operands."""
+        mark = mark or (lambda name: None)
+        T, k, d, f, E = self.T, self.k, self.d, self.f, self.E
+        rows, G = T * k + T, E + 1
+        moe_combine_backward(dout, self.y, self.pos, self.w, T * k, self.dy, self.dw, stream)
+        fp8_quant_1x128_pow2(self.dy, self.dyq, self.dys, stream)
+        mark("combine_bwd")
+        grouped_gemm_fp8_down(self.dyq, self.dys, self.offsets, weights_t.w2q, weights_t.w2s, self.dh, stream)
+        mark("dgrad_w2")
+        moe_swiglu_backward(self.gu, self.gus, self.dh, self.offsets, G, self.dgu, self.dgus,
+                            self.dgu_t, self.dgu_ts, self.h_t, self.h_ts, stream)
+        mark("swiglu_bwd")
+        grouped_gemm_fp8_down(self.dgu, self.dgus, self.offsets, weights_t.w13q, weights_t.w13s,
+                              self.dx_rows, stream)
+        moe_combine(self.dx_rows, self.pos, self.ones, T * k, self.dx, stream)
+        mark("dgrad_w13")
+        moe_regroup_128x1(self.offsets, G, rows, self.dy_t, self.dy_ts, x_bf16=self.dy, stream=stream)
+        moe_regroup_128x1(self.offsets, G, rows, self.x_t, self.x_ts, xq=self.xq, xs=self.xs,
+                          row_src=self.row_token, stream=stream)
+        mark("regroup")
+        grouped_gemm_fp8_wgrad(self.dy_t, self.dy_ts, self.h_t, self.h_ts, self.offsets, G, rows,
+                               self.dw2, stream)
+        mark("wgrad_w2")
+        grouped_gemm_fp8_wgrad(self.dgu_t, self.dgu_ts, self.x_t, self.x_ts, self.offsets, G, rows,
+                               self.dw13, stream)
+        mark("wgrad_w13")
+        return self.dx, self.dw13, self.dw2, self.dw
 
     def update_bias(self, bias, gamma, stream=None):
         """After forward(): one step of the balancing controller on ``bias``

@@ -50,6 +50,13 @@ SIGNATURES = {
     "fp8_quant_128x128_pow2": (I, [P, I, I, P, P, P]),
     "grouped_gemm_fp8_up_e8m0": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P]),
     "grouped_gemm_fp8_down_e8m0": (I, [P, P, P, I, I, I, I, P, P, P, P]),
+    "moe_transpose_fp8_blocks": (I, [P, P, I, I, I, P, P, P]),
+    "moe_combine_backward": (I, [P, P, P, P, I, I, I, ctypes.c_int32, P, P, P]),
+    "moe_wgrad_columns": (I, [I, I]),
+    "moe_regroup_128x1": (I, [P, P, P, P, P, I, I, I, P, P, P]),
+    "moe_swiglu_backward": (I, [P, P, P, P, I, I, I, P, P, P, P, P, P, P]),
+    "grouped_gemm_fp8_wgrad": (I, [P, P, P, P, P, I, I, I, I, P, P]),
+    "grouped_gemm_fp8_up_train": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P, P, P]),
     "moe_status_string": (ctypes.c_char_p, [I]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -84,4 +91,4 @@ def header_symbols():
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(?:moe_status|size_t|const char\*)\s+(\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(?:moe_status|size_t|int|const char\*)\s+(\w+)\s*\(", text)))

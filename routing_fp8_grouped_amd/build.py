@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 SOURCES = ["api.cpp", "quant.hip", "route.hip", "permute.hip", "gemm.hip", "gemm_small.hip",
-           "combine.hip", "balance.hip"]
+           "combine.hip", "balance.hip", "backward.hip", "wgrad.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 

@@ -303,6 +303,26 @@ moe_status grouped_gemm_fp8_up_e8m0(const uint8_t* aq, const float* as, int a_ro
                       hs, true, stream);
 }
 
+moe_status grouped_gemm_fp8_up_train(const uint8_t* aq, const float* as, int a_rows,
+                                     const int32_t* row_src, const int32_t* offsets, int n_groups,
+                                     int total_rows, int d, int f, const uint8_t* w13,
+                                     const float* w13_s, uint8_t* h, float* hs, uint8_t* gu,
+                                     float* gus, void* stream) {
+  clear_error();
+  moe_status s = check_gemm_shape(n_groups, total_rows, d, f);
+  if (s != MOE_OK || total_rows == 0) return s;
+  s = check_up(d, aq, as, a_rows, row_src, offsets, total_rows, w13, w13_s, h, hs);
+  if (s != MOE_OK) return s;
+  REQUIRE_PTR(gu);
+  REQUIRE_PTR4(gus);
+  if ((uint64_t)total_rows * (uint64_t)(2 * f) > 0xFFFFFFFFull)
+    return fail(MOE_ERR_UNSUPPORTED, "total_rows*2f exceeds 4 GiB");
+  return hip_status(moe::launch_gemm_up(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d,
+                                        f, w13, w13_s, h, hs, false, static_cast<hipStream_t>(stream),
+                                        gu, gus),
+                    "grouped_gemm_fp8_up_train launch");
+}
+
 moe_status grouped_gemm_fp8_down(const uint8_t* h, const float* hs, const int32_t* offsets,
                                  int n_groups, int total_rows, int d, int f, const uint8_t* w2,
                                  const float* w2_s, uint16_t* y, void* stream) {
@@ -337,6 +357,136 @@ moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, int a_row
   return hip_status(moe::launch_gemm_down(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y,
                                           false, st),
                     "grouped_gemm_fp8_swiglu launch (down)");
+}
+
+// ---- backward ----
+
+moe_status moe_transpose_fp8_blocks(const uint8_t* w, const float* ws, int n_matrices, int N, int K,
+                                    uint8_t* wt, float* wts, void* stream) {
+  clear_error();
+  REQUIRE(n_matrices >= 0, "n_matrices=%d is negative", n_matrices);
+  REQUIRE(N >= 128 && N % 128 == 0, "N=%d must be a positive multiple of 128", N);
+  REQUIRE(K >= 128 && K % 128 == 0, "K=%d must be a positive multiple of 128", K);
+  if (n_matrices == 0) return MOE_OK;
+  if (n_matrices > 65535 || N / 128 > 65535)
+    return fail(MOE_ERR_UNSUPPORTED, "n_matrices=%d or N/128 exceeds 65535", n_matrices);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR4(ws);
+  REQUIRE_PTR(wt);
+  REQUIRE_PTR4(wts);
+  REQUIRE(w != wt, "in-place transposition is not supported");
+  return hip_status(moe::launch_transpose_blocks(w, ws, n_matrices, N, K, wt, wts,
+                                                 static_cast<hipStream_t>(stream)),
+                    "moe_transpose_fp8_blocks launch");
+}
+
+moe_status moe_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
+                                const float* w, int T, int k, int d, int32_t shared_row0,
+                                uint16_t* dy, float* dw, void* stream) {
+  clear_error();
+  REQUIRE(T >= 0, "T=%d is negative", T);
+  REQUIRE(k >= 1 && k <= 16, "k=%d must be in [1, 16]", k);
+  REQUIRE(d >= 128 && d % 128 == 0, "d=%d must be a positive multiple of 128", d);
+  REQUIRE(shared_row0 >= -1, "shared_row0=%d must be >= -1", shared_row0);
+  if (T == 0) return MOE_OK;
+  REQUIRE(T <= INT32_MAX / (k + 1), "T*(k+1) overflows int32");
+  REQUIRE_PTR(dout);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR4(pos);
+  REQUIRE_PTR4(w);
+  REQUIRE_PTR(dy);
+  REQUIRE_PTR4(dw);
+  return hip_status(moe::launch_combine_backward(dout, y, pos, w, T, k, d, shared_row0, dy, dw,
+                                                 static_cast<hipStream_t>(stream)),
+                    "moe_combine_backward launch");
+}
+
+int moe_wgrad_columns(int total_rows, int n_groups) {
+  if (total_rows < 0 || n_groups < 1) return 0;
+  const long long c = 128LL * moe::wgrad_blocks_bound(total_rows, n_groups);
+  return c > INT32_MAX ? 0 : (int)c;
+}
+
+namespace {
+
+moe_status check_wgrad_layout(const int32_t* offsets, int n_groups, int total_rows, int C) {
+  REQUIRE(n_groups >= 1, "n_groups=%d must be >= 1", n_groups);
+  if (n_groups > 1024) return fail(MOE_ERR_UNSUPPORTED, "n_groups=%d > 1024", n_groups);
+  REQUIRE(total_rows >= 0, "total_rows=%d is negative", total_rows);
+  REQUIRE(C >= 128 && C % 128 == 0, "columns=%d must be a positive multiple of 128", C);
+  if (moe::wgrad_blocks_bound(total_rows, n_groups) > 65535)
+    return fail(MOE_ERR_UNSUPPORTED, "more than 65535 padded row blocks");
+  if ((uint64_t)C * (uint64_t)moe_wgrad_columns(total_rows, n_groups) > 0xFFFFFFFFull)
+    return fail(MOE_ERR_UNSUPPORTED, "the K-major operand exceeds 4 GiB");
+  REQUIRE_PTR4(offsets);
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_regroup_128x1(const uint8_t* xq, const float* xs, const uint16_t* x_bf16,
+                             const int32_t* row_src, const int32_t* offsets, int n_groups,
+                             int total_rows, int C, uint8_t* out, float* out_s, void* stream) {
+  clear_error();
+  moe_status s = check_wgrad_layout(offsets, n_groups, total_rows, C);
+  if (s != MOE_OK || total_rows == 0) return s;
+  REQUIRE((xq != nullptr) != (x_bf16 != nullptr), "exactly one of xq and x_bf16 must be given");
+  if (xq) {
+    REQUIRE_PTR(xq);
+    REQUIRE_PTR4(xs);
+    REQUIRE_ALIGNED4_OR_NULL(row_src);
+  } else {
+    REQUIRE_PTR(x_bf16);
+    REQUIRE(row_src == nullptr, "row_src applies to the FP8 source only");
+  }
+  REQUIRE_PTR(out);
+  REQUIRE_PTR4(out_s);
+  return hip_status(moe::launch_regroup_128x1(xq, xs, x_bf16, row_src, offsets, n_groups, total_rows, C,
+                                              moe_wgrad_columns(total_rows, n_groups), out, out_s,
+                                              static_cast<hipStream_t>(stream)),
+                    "moe_regroup_128x1 launch");
+}
+
+moe_status moe_swiglu_backward(const uint8_t* gu, const float* gus, const uint16_t* dh,
+                               const int32_t* offsets, int n_groups, int total_rows, int f,
+                               uint8_t* dgu, float* dgus, uint8_t* dgu_t, float* dgu_ts,
+                               uint8_t* h_t, float* h_ts, void* stream) {
+  clear_error();
+  moe_status s = check_wgrad_layout(offsets, n_groups, total_rows, 2 * f);
+  if (s != MOE_OK || total_rows == 0) return s;
+  REQUIRE(f >= 128 && f % 128 == 0, "f=%d must be a positive multiple of 128", f);
+  REQUIRE_PTR(gu);
+  REQUIRE_PTR4(gus);
+  REQUIRE_PTR(dh);
+  REQUIRE_PTR(dgu);
+  REQUIRE_PTR4(dgus);
+  REQUIRE_PTR(dgu_t);
+  REQUIRE_PTR4(dgu_ts);
+  REQUIRE_PTR(h_t);
+  REQUIRE_PTR4(h_ts);
+  return hip_status(moe::launch_swiglu_backward(gu, gus, dh, offsets, n_groups, total_rows, f,
+                                                moe_wgrad_columns(total_rows, n_groups), dgu, dgus,
+                                                dgu_t, dgu_ts, h_t, h_ts, static_cast<hipStream_t>(stream)),
+                    "moe_swiglu_backward launch");
+}
+
+moe_status grouped_gemm_fp8_wgrad(const uint8_t* a_t, const float* a_ts, const uint8_t* b_t,
+                                  const float* b_ts, const int32_t* offsets, int n_groups,
+                                  int total_rows, int M, int N, float* dw, void* stream) {
+  clear_error();
+  moe_status s = check_wgrad_layout(offsets, n_groups, total_rows, M > N ? M : N);
+  if (s != MOE_OK) return s;
+  REQUIRE(M >= 128 && M % 128 == 0, "M=%d must be a positive multiple of 128", M);
+  REQUIRE(N >= 128 && N % 128 == 0, "N=%d must be a positive multiple of 128", N);
+  REQUIRE_PTR(a_t);
+  REQUIRE_PTR4(a_ts);
+  REQUIRE_PTR(b_t);
+  REQUIRE_PTR4(b_ts);
+  REQUIRE_PTR(dw);
+  return hip_status(moe::launch_wgrad(a_t, a_ts, b_t, b_ts, offsets, n_groups, M, N,
+                                      moe_wgrad_columns(total_rows, n_groups), dw,
+                                      static_cast<hipStream_t>(stream)),
+                    "grouped_gemm_fp8_wgrad launch");
 }
 
 moe_status moe_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k, int d,

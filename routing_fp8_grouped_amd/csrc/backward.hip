@@ -1,0 +1,410 @@
+// Backward of the MoE layer around the expert GEMMs (the "DeepSeek-V3" summary
+// page, section 6 "FP8 mixed-precision training": Fprop, Dgrad and Wgrad all in
+// FP8; the book's chapter 17 "One linear layer creates three GEMMs", "SwiGLU
+// recomputation", and the regrouping of 1x128 tiles into 128x1 tiles with
+// power-of-two scales; chapter 16 "Why transposition is not trivial").
+//
+//   transpose_blocks_kernel   FP8 weights [N, K] -> [K, N] with their 128x128
+//                             block scales (once, offline): Dgrad multiplies
+//                             by W rather than W^T
+//   combine_backward_kernel   dY rows of the experts and the gate gradients
+//   regroup_128x1_kernel      a per-expert 128x1 (along rows), power-of-two,
+//                             transposed FP8 copy of an operand of Wgrad
+//   swiglu_backward_kernel    SiLU(g)*u recomputed from the forward's FP8 cache
+//                             of [G, U]; dG, dU; their 1x128 FP8 copy for Dgrad
+//                             and the transposed 128x1 copies of [dG, dU] and H
+//                             for Wgrad
+//
+// Transposed operands of Wgrad ("K-major" layout): row c holds column c of the
+// original for all rows of all experts, expert e occupying the 128-aligned
+// column range [128 pb[e], 128 pb[e+1]) with pb[e] = sum over earlier experts of
+// ceil(rows / 128); padding columns are zero codes.  Their scales are
+// [Kp/128, C]: one per column and 128-row block.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int BW_MAX_GROUPS = 1024;
+
+// E4M3 code -> FP32 (exact; the code is OCP E4M3FN as written by the quantisers).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+
+// pb[e] = sum over groups e' < e of ceil(rows(e') / 128), pb[n_groups] = total.
+// One wave computes it into LDS; the caller synchronises.
+__device__ __forceinline__ void padded_block_prefix(const int32_t* __restrict__ offsets, int n_groups,
+                                                    int* pb, int lane) {
+  int carry = 0;
+  for (int base = 0; base < n_groups; base += 64) {
+    const int g = base + lane;
+    int nb = 0;
+    if (g < n_groups) nb = (offsets[g + 1] - offsets[g] + 127) >> 7;
+    int v = nb;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    if (g < n_groups) pb[g + 1] = carry + v;
+    carry += __shfl(v, 63);
+  }
+  if (lane == 0) pb[0] = 0;
+}
+
+// Group holding padded block blk (pb non-decreasing; empty groups are skipped).
+__device__ __forceinline__ int block_group(const int* pb, int n_groups, int blk) {
+  int a = 0, b = n_groups - 1;
+  while (a < b) {
+    const int mid = (a + b + 1) >> 1;
+    if (pb[mid] <= blk) a = mid; else b = mid - 1;
+  }
+  return a;
+}
+
+// ---- weights: [G][N][K] -> [G][K][N], scales [G][N/128][K/128] -> [G][K/128][N/128]
+__global__ __launch_bounds__(256) void transpose_blocks_kernel(const uint8_t* __restrict__ w,
+                                                               const float* __restrict__ ws, int N,
+                                                               int K, uint8_t* __restrict__ wt,
+                                                               float* __restrict__ wts) {
+  __shared__ uint8_t tile[128][129];
+  const int kb = blockIdx.x, nb = blockIdx.y, g = blockIdx.z, t = threadIdx.x;
+  const size_t src0 = (size_t)g * N * K + (size_t)nb * 128 * K + (size_t)kb * 128;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int chunk = t + 256 * i, r = chunk >> 3, c16 = chunk & 7;
+    const uint4 v = *reinterpret_cast<const uint4*>(w + src0 + (size_t)r * K + c16 * 16);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tile[r][c16 * 16 + j] = (uint8_t)(u[j >> 2] >> (8 * (j & 3)));
+  }
+  __syncthreads();
+  const size_t dst0 = (size_t)g * N * K + (size_t)kb * 128 * N + (size_t)nb * 128;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int chunk = t + 256 * i, rr = chunk >> 3, c16 = chunk & 7;
+    uint32_t u[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) u[j >> 2] |= (uint32_t)tile[c16 * 16 + j][rr] << (8 * (j & 3));
+    *reinterpret_cast<uint4*>(wt + dst0 + (size_t)rr * N + c16 * 16) = make_uint4(u[0], u[1], u[2], u[3]);
+  }
+  if (t == 0)
+    wts[((size_t)g * (K / 128) + kb) * (N / 128) + nb] = ws[((size_t)g * (N / 128) + nb) * (K / 128) + kb];
+}
+
+// ---- combine backward: one workgroup per token ----
+// dy[pos[t][j]] = BF16(w[t][j] * dout[t]); dy[shared_row0 + t] = dout[t];
+// dw[t][j] = sum_c dout[t][c] * y[pos[t][j]][c] in FP32.
+__global__ __launch_bounds__(256) void combine_backward_kernel(
+    const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y, const int32_t* __restrict__ pos,
+    const float* __restrict__ w, int k, int d, int shared_row0, uint16_t* __restrict__ dy,
+    float* __restrict__ dw) {
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* go = dout + (size_t)t * d;
+  const int n8 = d / 8;
+  for (int j = 0; j < k; ++j) {
+    const int row = pos[t * k + j];
+    const float wt = w[t * k + j];
+    float part = 0.0f;
+    for (int c = tid; c < n8; c += 256) {
+      const uint4 a = *reinterpret_cast<const uint4*>(go + c * 8);
+      const uint4 b = *reinterpret_cast<const uint4*>(y + (size_t)row * d + c * 8);
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a0 = bf16_to_f32((uint16_t)(av[i] & 0xFFFFu)), a1 = bf16_to_f32((uint16_t)(av[i] >> 16));
+        const float b0 = bf16_to_f32((uint16_t)(bv[i] & 0xFFFFu)), b1 = bf16_to_f32((uint16_t)(bv[i] >> 16));
+        part = fmaf(a0, b0, part);
+        part = fmaf(a1, b1, part);
+        o[i] = (uint32_t)f32_to_bf16(wt * a0) | ((uint32_t)f32_to_bf16(wt * a1) << 16);
+      }
+      *reinterpret_cast<uint4*>(dy + (size_t)row * d + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    if (lane == 0) red[wave] = part;
+    __syncthreads();
+    if (tid == 0) dw[t * k + j] = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+  }
+  if (shared_row0 >= 0)
+    for (int c = tid; c < n8; c += 256)
+      *reinterpret_cast<uint4*>(dy + (size_t)(shared_row0 + t) * d + c * 8) =
+          *reinterpret_cast<const uint4*>(go + c * 8);
+}
+
+// ---- 128x1 regrouping into the K-major layout ----
+// Workgroup (cb, blk): columns [128 cb, 128 cb + 128) of padded block blk.
+// FP8IN: the source is a 1x128 FP8 tensor (codes + scales) whose row r of the
+// grouped order is row row_src[r] (or r when row_src is null); otherwise a BF16
+// tensor in grouped order.  Values are dequantised in FP32, each column's
+// 128-row amax gives a power-of-two scale, codes are E4M3(x / scale).
+template <bool FP8IN>
+__global__ __launch_bounds__(256) void regroup_128x1_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint16_t* __restrict__ xb,
+    const int32_t* __restrict__ row_src, const int32_t* __restrict__ offsets, int n_groups, int C,
+    int Kp, uint8_t* __restrict__ out, float* __restrict__ out_s) {
+  __shared__ int pb[BW_MAX_GROUPS + 1];
+  __shared__ float tile[128][129];
+  __shared__ float colmax[2][128];
+  const int tid = threadIdx.x, cb = blockIdx.x, blk = blockIdx.y;
+  if (tid < 64) padded_block_prefix(offsets, n_groups, pb, tid);
+  __syncthreads();
+  if (blk >= pb[n_groups]) return;   // uniform
+  const int e = block_group(pb, n_groups, blk);
+  const int row0 = offsets[e] + (blk - pb[e]) * 128;
+  const int nrows = min(128, offsets[e + 1] - row0);
+  {
+    const int r = tid >> 1, half = tid & 1;
+    float v[64];
+    if (r < nrows) {
+      if (FP8IN) {
+        const int src = row_src ? row_src[row0 + r] : row0 + r;
+        const float s = xs[(size_t)src * (C / 128) + cb];
+        const uint8_t* p = xq + (size_t)src * C + cb * 128 + half * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 q = *reinterpret_cast<const uint4*>(p + i * 16);
+          const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[i * 16 + j] = e4m3_to_f32((u[j >> 2] >> (8 * (j & 3))) & 0xFFu) * s;
+        }
+      } else {
+        const uint16_t* p = xb + (size_t)(row0 + r) * C + cb * 128 + half * 64;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint4 q = *reinterpret_cast<const uint4*>(p + i * 8);
+          const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[i * 8 + 2 * j] = bf16_to_f32((uint16_t)(u[j] & 0xFFFFu));
+            v[i * 8 + 2 * j + 1] = bf16_to_f32((uint16_t)(u[j] >> 16));
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) v[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) tile[r][half * 64 + i] = v[i];
+  }
+  __syncthreads();
+  const int c = tid & 127, part = tid >> 7;
+  float amax = 0.0f;
+  for (int r = part * 64; r < part * 64 + 64; ++r) amax = fmaxf(amax, fabsf(tile[r][c]));
+  colmax[part][c] = amax;
+  __syncthreads();
+  const float s = scale_from_amax_pow2(fmaxf(colmax[0][c], colmax[1][c]));
+  uint8_t* dst = out + (size_t)(cb * 128 + c) * Kp + (size_t)blk * 128 + part * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = part * 64 + i * 16;
+    uint32_t u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      u[j] = f32x4_to_e4m3(tile[r + 4 * j][c] / s, tile[r + 4 * j + 1][c] / s, tile[r + 4 * j + 2][c] / s,
+                           tile[r + 4 * j + 3][c] / s);
+    *reinterpret_cast<uint4*>(dst + i * 16) = make_uint4(u[0], u[1], u[2], u[3]);
+  }
+  if (part == 0) out_s[(size_t)blk * C + cb * 128 + c] = s;
+}
+
+// ---- SwiGLU backward ----
+// Workgroup (cb, blk): h-columns [128 cb, 128 cb + 128) of padded block blk.
+// From the cache, g and u are the codes times their 1x128 scales (FP32);
+// s = sigmoid(g), h = g s u, dG = dH u s (1 + g (1 - s)), dU = dH g s are
+// evaluated in FP64 and rounded once to FP32.  Outputs: [dG, dU] with 1x128
+// power-of-two scales in row order (the Dgrad operand), and the K-major 128x1
+// copies of [dG, dU] ([2f, Kp]) and of h ([f, Kp]) (the Wgrad operands).
+struct SwigluVals {
+  float h, dg, du;
+};
+
+__device__ __forceinline__ SwigluVals swiglu_bwd_vals(float g, float u, float dh) {
+  const double gd = g, ud = u, dhd = dh;
+  const double s = 1.0 / (1.0 + exp(-gd));
+  SwigluVals r;
+  r.h = (float)(gd * s * ud);
+  r.dg = (float)(dhd * ud * s * (1.0 + gd * (1.0 - s)));
+  r.du = (float)(dhd * gd * s);
+  return r;
+}
+
+__global__ __launch_bounds__(256) void swiglu_backward_kernel(
+    const uint8_t* __restrict__ guq, const float* __restrict__ gus, const uint16_t* __restrict__ dh,
+    const int32_t* __restrict__ offsets, int n_groups, int f, int Kp, uint8_t* __restrict__ dguq,
+    float* __restrict__ dgus, uint8_t* __restrict__ dgut, float* __restrict__ dguts,
+    uint8_t* __restrict__ ht, float* __restrict__ hts) {
+  __shared__ int pb[BW_MAX_GROUPS + 1];
+  __shared__ uint8_t gq[128][128];
+  __shared__ uint8_t uq[128][128];
+  __shared__ uint16_t dhs[128][130];
+  __shared__ float gsc[128], usc[128];
+  __shared__ uint32_t rmax_g[128], rmax_u[128];   // FP32 bits of non-negative row amax
+  __shared__ float cmax[3][2][128];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2][128][128];
+  const int tid = threadIdx.x, cb = blockIdx.x, blk = blockIdx.y;
+  if (tid < 64) padded_block_prefix(offsets, n_groups, pb, tid);
+  if (tid < 128) {
+    rmax_g[tid] = 0u;
+    rmax_u[tid] = 0u;
+  }
+  __syncthreads();
+  if (blk >= pb[n_groups]) return;   // uniform
+  const int e = block_group(pb, n_groups, blk);
+  const int row0 = offsets[e] + (blk - pb[e]) * 128;
+  const int nrows = min(128, offsets[e + 1] - row0);
+  const int nsc = 2 * f / 128;
+  {
+    const int r = tid >> 1, half = tid & 1;
+    if (r < nrows) {
+      const size_t rowi = (size_t)(row0 + r);
+      const uint8_t* pg = guq + rowi * 2 * f + cb * 128 + half * 64;
+      const uint8_t* pu = pg + f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<uint4*>(&gq[r][half * 64 + i * 16]) = *reinterpret_cast<const uint4*>(pg + i * 16);
+        *reinterpret_cast<uint4*>(&uq[r][half * 64 + i * 16]) = *reinterpret_cast<const uint4*>(pu + i * 16);
+      }
+      const uint16_t* pd = dh + rowi * f + cb * 128 + half * 64;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 q = *reinterpret_cast<const uint4*>(pd + i * 8);
+        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dhs[r][half * 64 + i * 8 + 2 * j] = (uint16_t)(u[j] & 0xFFFFu);
+          dhs[r][half * 64 + i * 8 + 2 * j + 1] = (uint16_t)(u[j] >> 16);
+        }
+      }
+      if (half == 0) {
+        gsc[r] = gus[rowi * nsc + cb];
+        usc[r] = gus[rowi * nsc + f / 128 + cb];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        gq[r][half * 64 + i] = 0;
+        uq[r][half * 64 + i] = 0;
+        dhs[r][half * 64 + i] = 0;
+      }
+      if (half == 0) gsc[r] = usc[r] = 0.0f;
+    }
+  }
+  __syncthreads();
+  // column layout: thread -> column c, rows part*64 .. +63
+  const int c = tid & 127, part = tid >> 7;
+  float mh = 0.0f, mg = 0.0f, mu = 0.0f;
+  for (int r = part * 64; r < part * 64 + 64; ++r) {
+    const SwigluVals v = swiglu_bwd_vals(e4m3_to_f32(gq[r][c]) * gsc[r], e4m3_to_f32(uq[r][c]) * usc[r],
+                                         bf16_to_f32(dhs[r][c]));
+    mh = fmaxf(mh, fabsf(v.h));
+    mg = fmaxf(mg, fabsf(v.dg));
+    mu = fmaxf(mu, fabsf(v.du));
+    atomicMax(&rmax_g[r], __float_as_uint(fabsf(v.dg)));
+    atomicMax(&rmax_u[r], __float_as_uint(fabsf(v.du)));
+  }
+  cmax[0][part][c] = mh;
+  cmax[1][part][c] = mg;
+  cmax[2][part][c] = mu;
+  __syncthreads();
+  const float sh = scale_from_amax_pow2(fmaxf(cmax[0][0][c], cmax[0][1][c]));
+  const float sg = scale_from_amax_pow2(fmaxf(cmax[1][0][c], cmax[1][1][c]));
+  const float su = scale_from_amax_pow2(fmaxf(cmax[2][0][c], cmax[2][1][c]));
+  uint8_t* oh = ht + (size_t)(cb * 128 + c) * Kp + (size_t)blk * 128 + part * 64;
+  uint8_t* og = dgut + (size_t)(cb * 128 + c) * Kp + (size_t)blk * 128 + part * 64;
+  uint8_t* ou = dgut + (size_t)(f + cb * 128 + c) * Kp + (size_t)blk * 128 + part * 64;
+#pragma unroll 1
+  for (int i = 0; i < 4; ++i) {
+    uint32_t wh[4], wg[4], wu[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float vh[4], vg[4], vu[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = part * 64 + i * 16 + j * 4 + q;
+        const SwigluVals v = swiglu_bwd_vals(e4m3_to_f32(gq[r][c]) * gsc[r], e4m3_to_f32(uq[r][c]) * usc[r],
+                                             bf16_to_f32(dhs[r][c]));
+        vh[q] = v.h;
+        vg[q] = v.dg;
+        vu[q] = v.du;
+        // row-major copy with the row's power-of-two scale
+        stage[0][r][c] = (uint8_t)(f32x2_to_e4m3(v.dg / scale_from_amax_pow2(__uint_as_float(rmax_g[r])), 0.0f) & 0xFFu);
+        stage[1][r][c] = (uint8_t)(f32x2_to_e4m3(v.du / scale_from_amax_pow2(__uint_as_float(rmax_u[r])), 0.0f) & 0xFFu);
+      }
+      wh[j] = f32x4_to_e4m3(vh[0] / sh, vh[1] / sh, vh[2] / sh, vh[3] / sh);
+      wg[j] = f32x4_to_e4m3(vg[0] / sg, vg[1] / sg, vg[2] / sg, vg[3] / sg);
+      wu[j] = f32x4_to_e4m3(vu[0] / su, vu[1] / su, vu[2] / su, vu[3] / su);
+    }
+    *reinterpret_cast<uint4*>(oh + i * 16) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    *reinterpret_cast<uint4*>(og + i * 16) = make_uint4(wg[0], wg[1], wg[2], wg[3]);
+    *reinterpret_cast<uint4*>(ou + i * 16) = make_uint4(wu[0], wu[1], wu[2], wu[3]);
+  }
+  if (part == 0) {
+    hts[(size_t)blk * f + cb * 128 + c] = sh;
+    dguts[(size_t)blk * 2 * f + cb * 128 + c] = sg;
+    dguts[(size_t)blk * 2 * f + f + cb * 128 + c] = su;
+  }
+  __syncthreads();
+  // row-major [dG, dU] codes and scales of the valid rows
+  for (int idx = tid; idx < 128 * 16; idx += 256) {
+    const int r = idx >> 4, q = idx & 15, which = q >> 3, c16 = q & 7;
+    if (r < nrows) {
+      const size_t rowi = (size_t)(row0 + r);
+      *reinterpret_cast<uint4*>(dguq + rowi * 2 * f + which * f + cb * 128 + c16 * 16) =
+          *reinterpret_cast<const uint4*>(&stage[which][r][c16 * 16]);
+    }
+  }
+  if (tid < 128 && tid < nrows) {
+    const size_t rowi = (size_t)(row0 + tid);
+    dgus[rowi * nsc + cb] = scale_from_amax_pow2(__uint_as_float(rmax_g[tid]));
+    dgus[rowi * nsc + f / 128 + cb] = scale_from_amax_pow2(__uint_as_float(rmax_u[tid]));
+  }
+}
+
+hipError_t launch_transpose_blocks(const uint8_t* w, const float* ws, int G, int N, int K, uint8_t* wt,
+                                   float* wts, hipStream_t stream) {
+  hipLaunchKernelGGL(transpose_blocks_kernel, dim3(K / 128, N / 128, G), dim3(256), 0, stream, w, ws, N, K,
+                     wt, wts);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
+                                   const float* w, int T, int k, int d, int shared_row0, uint16_t* dy,
+                                   float* dw, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_backward_kernel, dim3(T), dim3(256), 0, stream, dout, y, pos, w, k, d,
+                     shared_row0, dy, dw);
+  return hipGetLastError();
+}
+
+int wgrad_blocks_bound(int total_rows, int n_groups) { return total_rows / 128 + n_groups; }
+
+hipError_t launch_regroup_128x1(const uint8_t* xq, const float* xs, const uint16_t* xb,
+                                const int32_t* row_src, const int32_t* offsets, int n_groups,
+                                int total_rows, int C, int Kp, uint8_t* out, float* out_s,
+                                hipStream_t stream) {
+  const dim3 grid(C / 128, wgrad_blocks_bound(total_rows, n_groups));
+  if (xq)
+    hipLaunchKernelGGL(regroup_128x1_kernel<true>, grid, dim3(256), 0, stream, xq, xs, xb, row_src, offsets,
+                       n_groups, C, Kp, out, out_s);
+  else
+    hipLaunchKernelGGL(regroup_128x1_kernel<false>, grid, dim3(256), 0, stream, xq, xs, xb, row_src, offsets,
+                       n_groups, C, Kp, out, out_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_backward(const uint8_t* guq, const float* gus, const uint16_t* dh,
+                                  const int32_t* offsets, int n_groups, int total_rows, int f, int Kp,
+                                  uint8_t* dguq, float* dgus, uint8_t* dgut, float* dguts, uint8_t* ht,
+                                  float* hts, hipStream_t stream) {
+  const dim3 grid(f / 128, wgrad_blocks_bound(total_rows, n_groups));
+  hipLaunchKernelGGL(swiglu_backward_kernel, grid, dim3(256), 0, stream, guq, gus, dh, offsets, n_groups, f,
+                     Kp, dguq, dgus, dgut, dguts, ht, hts);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -68,6 +68,8 @@ struct GemmArgs {
   uint8_t* h;               // stage 1 out [rows, f]
   float* hs;                // stage 1 out [rows, f/128]
   uint16_t* y;              // stage 2 out [rows, N]
+  uint8_t* gu;              // stage 1, optional: FP8 cache of [G, U] [rows, 2f] (1x128 tiles)
+  float* gus;               // its scales [rows, 2f/128]
 };
 
 // LDS layout of a 128-byte operand row r: its 16-byte chunk c sits at chunk
@@ -256,6 +258,42 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& p, const Tile& c
   const int nhs = p.f / 128;
   constexpr int SEND = WN == 0 ? 4 : 0;   // sub-tile columns sent to the partner
   constexpr int KEEP = WN == 0 ? 0 : 4;   // sub-tile columns finished here
+  if (p.gu) {
+    // the SwiGLU input for the backward: this wave's 64 rows x 128 columns of
+    // G (WN = 0) or U (WN = 1) are exactly 1x128 tiles; quantised with the
+    // forward's rule, staged through the wave's own LDS region, stored by rows
+    unsigned char* Q = reinterpret_cast<unsigned char*>(mine);
+    const int ngs = 2 * nhs;
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float a = 0.0f;
+#pragma unroll
+        for (int ns = 0; ns < 8; ++ns) a = fmaxf(a, fabsf(acc[ms][ns][e]));
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+        const float sc = tile_scale<POW2>(a);
+        const float rs = recip(sc);
+        const int rt = wm * 64 + ms * 16 + g16 * 4 + e;
+        if (r16 == 0 && rt < cur.rows_valid) p.gus[(size_t)(cur.row0 + rt) * ngs + WN * nhs + cur.n] = sc;
+#pragma unroll
+        for (int ns = 0; ns < 8; ++ns)
+          Q[(ms * 16 + g16 * 4 + e) * 128 + ns * 16 + r16] =
+              (unsigned char)(f32x2_to_e4m3(div_by(acc[ms][ns][e], sc, rs), 0.0f) & 0xFFu);
+      }
+    wave_sync_lds();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int idx = it * 64 + lane;
+      const int rl = idx >> 3, cq = idx & 7;
+      const int rt = wm * 64 + rl;
+      const uint4 v = *reinterpret_cast<const uint4*>(Q + rl * 128 + cq * 16);
+      if (rt < cur.rows_valid)
+        *reinterpret_cast<uint4*>(p.gu + (size_t)(cur.row0 + rt) * 2 * p.f + WN * p.f + cur.n * 128 + cq * 16) = v;
+    }
+    wave_sync_lds();
+  }
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     __builtin_amdgcn_sched_barrier(0);
@@ -613,8 +651,10 @@ static int num_cus() {
 hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const int32_t* row_src,
                           const int32_t* offsets, int n_groups, int total_rows, int d, int f,
                           const uint8_t* w13, const float* w13_s, uint8_t* h, float* hs,
-                          bool e8m0, hipStream_t stream) {
-  if (total_rows <= 16 * n_groups)   // few rows per group: stream the weights
+                          bool e8m0, hipStream_t stream, uint8_t* gu, float* gus) {
+  // few rows per group: stream the weights (the tiled kernel alone writes the
+  // [G, U] cache)
+  if (total_rows <= 16 * n_groups && gu == nullptr)
     return launch_gemm_up_small(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d, f, w13,
                                 w13_s, h, hs, e8m0, stream);
   const int grid = ((num_cus() + 7) / 8) * 8;
@@ -633,6 +673,8 @@ hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const 
   s1.f = f;
   s1.h = h;
   s1.hs = hs;
+  s1.gu = gu;
+  s1.gus = gus;
   if (e8m0)
     hipLaunchKernelGGL((grouped_gemm_kernel<true, true>), dim3(grid), dim3(NTHR), 0, stream, s1, offsets);
   else

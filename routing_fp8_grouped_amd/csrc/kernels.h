@@ -27,7 +27,7 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const uint8_t
 hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const int32_t* row_src,
                           const int32_t* offsets, int n_groups, int total_rows, int d, int f,
                           const uint8_t* w13, const float* w13_s, uint8_t* h, float* hs,
-                          bool e8m0, hipStream_t stream);
+                          bool e8m0, hipStream_t stream, uint8_t* gu = nullptr, float* gus = nullptr);
 hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* offsets, int n_groups,
                             int total_rows, int d, int f, const uint8_t* w2, const float* w2_s,
                             uint16_t* y, bool e8m0, hipStream_t stream);
@@ -45,6 +45,26 @@ hipError_t launch_gemm_down_small(const uint8_t* h, const float* hs, const int32
 
 hipError_t launch_bias_update(const int32_t* offsets, int E, float gamma, float* bias,
                               hipStream_t stream);
+
+// Backward around the expert GEMMs (backward.hip).
+hipError_t launch_transpose_blocks(const uint8_t* w, const float* ws, int G, int N, int K, uint8_t* wt,
+                                   float* wts, hipStream_t stream);
+hipError_t launch_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
+                                   const float* w, int T, int k, int d, int shared_row0, uint16_t* dy,
+                                   float* dw, hipStream_t stream);
+int wgrad_blocks_bound(int total_rows, int n_groups);
+hipError_t launch_regroup_128x1(const uint8_t* xq, const float* xs, const uint16_t* xb,
+                                const int32_t* row_src, const int32_t* offsets, int n_groups,
+                                int total_rows, int C, int Kp, uint8_t* out, float* out_s,
+                                hipStream_t stream);
+hipError_t launch_swiglu_backward(const uint8_t* guq, const float* gus, const uint16_t* dh,
+                                  const int32_t* offsets, int n_groups, int total_rows, int f, int Kp,
+                                  uint8_t* dguq, float* dgus, uint8_t* dgut, float* dguts, uint8_t* ht,
+                                  float* hts, hipStream_t stream);
+
+hipError_t launch_wgrad(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
+                        const int32_t* offsets, int n_groups, int M, int N, int Kp, float* out,
+                        hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k,
                           int d, int shared_row0, uint16_t* out, hipStream_t stream);

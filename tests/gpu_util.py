@@ -155,6 +155,31 @@ def gemm_noise(aq_rows, as_rows, wq, ws, acc):
             + kb * 2.0 ** -24 * np.abs(acc))
 
 
+# The MFMA's error per 128-product block also scales with the block's largest
+# product (its sum is formed on the exponent of the largest term): over 131,072
+# outputs of 56-block chains on uniform codes, Gaussian codes and 128x1 tiles
+# of tokens with log-normal amplitudes, |error| / sqrt(sum over blocks of
+# (max|a b| * s)^2) had RMS 3.6e-5 .. 6.8e-5 and maximum 2.1e-4 .. 3.4e-4,
+# whatever the spread of magnitudes inside a block (where the model above, in
+# sum|a b|, does not hold).  The bound takes 8e-4.
+MAXPROD_FACTOR = 8e-4
+
+
+def block_max_products(aq, sa, bq, sb):
+    """sqrt over K blocks of (max over the block of |a b| * sa * sb)^2 [M, N],
+    both operands scaled per row and block (sa [M, K/128], sb [N, K/128])."""
+    a = np.abs(ofp8.e4m3_decode(np.asarray(aq))); b = np.abs(ofp8.e4m3_decode(np.asarray(bq)))
+    sa = np.asarray(sa, np.float64); sb = np.asarray(sb, np.float64)
+    M, N = a.shape[0], b.shape[0]
+    out = np.zeros((M, N))
+    for kb in range(a.shape[1] // 128):
+        blk = slice(kb * 128, (kb + 1) * 128)
+        for m0 in range(0, M, 32):
+            mp = np.max(a[m0:m0 + 32, None, blk] * b[None, :, blk], axis=2)
+            out[m0:m0 + 32] += (mp * sa[m0:m0 + 32, kb:kb + 1] * sb[None, :, kb]) ** 2
+    return np.sqrt(out)
+
+
 def e4m3_spacing(v):
     """Distance between neighbouring E4M3 values at magnitude |v|."""
     v = np.abs(np.asarray(v, np.float64))
@@ -187,36 +212,46 @@ def pow2_scale_choices(h, eh):
     return oquant.scale_from_amax(lo, "pow2"), oquant.scale_from_amax(hi, "pow2")
 
 
-def h_code_ambiguity(aq_rows, as_rows, w13q, w13s, g, u, h, hs, rule="fp32"):
-    """(amb, step) for the rows' h codes: amb marks elements whose scaled value
-    lies within the noise band of a rounding midpoint; step bounds how far
-    (in scaled units) a valid code of such an element can be from the oracle's:
-    the GPU code rounds some value inside the band, so the two codes differ by
-    at most twice the band plus one grid spacing (near zero the band can cover
-    several subnormal steps).  With the power-of-two rule a tile whose scale
-    may legitimately be the next power up or down is ambiguous as a whole: its
-    GPU values sit on a grid up to twice as coarse, i.e. within twice the
-    band plus three spacings of the oracle's (in the oracle's scaled units)."""
-    g = np.asarray(g, np.float64); u = np.asarray(u, np.float64); h = np.asarray(h, np.float64)
-    eh = h_noise(aq_rows, as_rows, w13q, w13s, g, u, h)
-    rows = h.shape[0]
-    ht = np.abs(h).reshape(rows, -1, 128)
-    et = eh.reshape(rows, -1, 128)
-    amax = ht.max(-1)
-    # the tile scale is amax/448 of equally noisy values
-    scale_rel = (np.max(ht + et, -1) - amax + np.max(et, -1)) / np.maximum(amax, 1e-300)
-    hsx = np.repeat(np.asarray(hs, np.float64), 128, axis=1)
-    y = np.abs(h) / hsx
-    band = eh / hsx + y * np.repeat(scale_rel, 128, axis=1)
+def code_ambiguity(v, ev, scales):
+    """(amb, step) for the 1x128 codes of values v [rows, C] whose GPU values may
+    differ by up to ev: amb marks elements whose scaled value lies within the
+    noise band of an E4M3 rounding midpoint (the tile scale, amax/448 of
+    equally noisy values, moves with them); step bounds how far in scaled
+    units a valid code of such an element can be from the oracle's: the GPU
+    code rounds some value inside the band, so the two differ by at most twice
+    the band plus one grid spacing (near zero the band can cover several
+    subnormal steps)."""
+    v = np.asarray(v, np.float64); ev = np.asarray(ev, np.float64)
+    rows = v.shape[0]
+    vt = np.abs(v).reshape(rows, -1, 128)
+    et = ev.reshape(rows, -1, 128)
+    amax = vt.max(-1)
+    scale_rel = (np.max(vt + et, -1) - amax + np.max(et, -1)) / np.maximum(amax, 1e-300)
+    sx = np.repeat(np.asarray(scales, np.float64), 128, axis=1)
+    y = np.abs(v) / sx
+    band = ev / sx + y * np.repeat(scale_rel, 128, axis=1)
     sp = e4m3_spacing(y)
     lo = np.floor(y / sp) * sp
     sp_below = e4m3_spacing(np.maximum(lo - sp / 4, 0.0))
     dist = np.minimum(np.abs(y - (lo + sp / 2)), np.abs(y - (lo - sp_below / 2)))
     step = 2.0 * band + e4m3_spacing(y + band)
-    amb = dist <= band
-    h_code_ambiguity.margin = dist / np.maximum(band, 1e-300)   # for failure reports
-    h_code_ambiguity.y = y
+    code_ambiguity.margin = dist / np.maximum(band, 1e-300)   # for failure reports
+    code_ambiguity.y = y
+    code_ambiguity.band = band
+    return dist <= band, step
+
+
+def h_code_ambiguity(aq_rows, as_rows, w13q, w13s, g, u, h, hs, rule="fp32"):
+    """code_ambiguity of the rows' h codes, with the noise of h propagated from
+    G and U.  With the power-of-two rule a tile whose scale may legitimately
+    be the next power up or down is ambiguous as a whole: its GPU values sit
+    on a grid up to twice as coarse, i.e. within twice the band plus three
+    spacings of the oracle's (in the oracle's scaled units)."""
+    g = np.asarray(g, np.float64); u = np.asarray(u, np.float64); h = np.asarray(h, np.float64)
+    eh = h_noise(aq_rows, as_rows, w13q, w13s, g, u, h)
+    amb, step = code_ambiguity(h, eh, hs)
     if rule == "pow2":
+        y, band = code_ambiguity.y, code_ambiguity.band
         s_lo, s_hi = pow2_scale_choices(h, eh)
         flip = np.repeat(s_lo != s_hi, 128, axis=1)
         amb = amb | flip
@@ -232,9 +267,9 @@ def check_h_codes(gh, hq, amb, step):
     same = (gh == hq) | (((gh & 0x7F) == 0) & ((hq & 0x7F) == 0))
     bad = ~same & ~amb
     if np.any(bad):
-        m = getattr(h_code_ambiguity, "margin", None)
+        m = getattr(code_ambiguity, "margin", None)
         if m is not None and m.shape == bad.shape:
-            yv = h_code_ambiguity.y
+            yv = code_ambiguity.y
             print("  codes outside the band: distance to midpoint / band =",
                   np.array2string(m[bad][:10], precision=3), "scaled value",
                   np.array2string(yv[bad][:10], precision=4), "gpu", gh[bad][:10], "oracle", hq[bad][:10],

@@ -31,6 +31,9 @@ def test_exports_every_declared_symbol(lib):
                              "grouped_gemm_fp8_down", "moe_combine", "moe_bias_update",
                              "fp8_quant_1x128_pow2", "fp8_quant_128x128_pow2",
                              "grouped_gemm_fp8_up_e8m0", "grouped_gemm_fp8_down_e8m0",
+                             "grouped_gemm_fp8_up_train", "moe_transpose_fp8_blocks",
+                             "moe_combine_backward", "moe_wgrad_columns", "moe_regroup_128x1",
+                             "moe_swiglu_backward", "grouped_gemm_fp8_wgrad",
                              "moe_status_string", "moe_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -177,3 +180,25 @@ def test_python_binding_requires_gpu_tensors():
     x = torch.zeros(4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         moe.fp8_quant_1x128(x, torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4, 1))
+
+
+def test_backward_validation(lib):
+    assert lib.moe_wgrad_columns(1000, 3) == 128 * (1000 // 128 + 3)
+    assert lib.moe_wgrad_columns(-1, 3) == 0 and lib.moe_wgrad_columns(10, 0) == 0
+    assert lib.moe_transpose_fp8_blocks(A, A, 2, 100, 128, A, A, None) == 1 and "N=100" in last(lib)
+    assert lib.moe_transpose_fp8_blocks(A, A, 2, 128, 128, A, A, None) == 1 and "in-place" in last(lib)
+    assert lib.moe_transpose_fp8_blocks(None, None, 0, 128, 128, None, None, None) == 0
+    assert lib.moe_combine_backward(A, A, A, A, 10, 0, 256, 80, A, A, None) == 1
+    assert lib.moe_combine_backward(A, A, A, MIS4, 10, 8, 256, 80, A, A, None) == 1
+    assert lib.moe_combine_backward(None, None, None, None, 0, 8, 256, 0, None, None, None) == 0
+    # exactly one source for the regrouping
+    assert lib.moe_regroup_128x1(A, A, A, None, A, 3, 100, 256, A, A, None) == 1 and "exactly one" in last(lib)
+    assert lib.moe_regroup_128x1(None, None, A, A, A, 3, 100, 256, A, A, None) == 1 and "row_src" in last(lib)
+    assert lib.moe_regroup_128x1(A, A, None, None, A, 3, 100, 100, A, A, None) == 1
+    assert lib.moe_regroup_128x1(A, A, None, None, A, 2000, 100, 256, A, A, None) == 2
+    assert lib.moe_swiglu_backward(A, A, A, A, 3, 100, 100, A, A, A, A, A, A, None) == 1
+    assert lib.moe_swiglu_backward(A, A, None, A, 3, 100, 128, A, A, A, A, A, A, None) == 1 and "dh is NULL" in last(lib)
+    assert lib.grouped_gemm_fp8_wgrad(A, A, A, A, A, 3, 100, 256, 100, A, None) == 1 and "N=100" in last(lib)
+    assert lib.grouped_gemm_fp8_wgrad(A, A, A, A, A, 3, 100, 256, 256, MIS, None) == 1
+    up = lambda gu=A: lib.grouped_gemm_fp8_up_train(A, A, 10, A, A, 257, 100, 256, 128, A, A, A, A, gu, A, None)
+    assert up(gu=None) == 1 and "gu is NULL" in last(lib)
