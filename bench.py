@@ -17,6 +17,9 @@ dense FP8 MFMA peak, timed with HIP events on the stream it runs on;
 ``e8m0_variant`` times the same workload once more with power-of-two scales on
 the hardware block-scaled MFMA (weights requantised with that rule, outside
 the timed region); the headline ``value`` is the FP32-scale method.
+``backward`` times the layer's backward (FP8 Dgrad and Wgrad, SwiGLU
+recomputed from the forward's FP8 cache) for one output gradient of the same
+batch, after a training forward outside the timed region.
 """
 
 import argparse
@@ -38,6 +41,7 @@ METRIC = "MoE-layer tokens/s at d=7168,E=256,k=8; FP8 grouped-GEMM % of MFMA pea
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense E4M3 MFMA
 HBM_PEAK_GBS = 8000.0
 STAGES = ["route", "quant", "permute", "gemm_up", "gemm_down", "combine"]
+BWD_STAGES = ["combine_bwd", "dgrad_w2", "swiglu_bwd", "dgrad_w13", "regroup", "wgrad_w2", "wgrad_w13"]
 
 
 def log(msg):
@@ -131,6 +135,22 @@ def timed_steps(layer, x, wg, b, W, steps):
     return (t1 - t0) * 1e3 / steps, stage_ms
 
 
+def timed_backward(layer, dout, Wt, steps):
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BWD_STAGES) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        it = iter(ev[s][1:])
+        layer.backward(dout, Wt, mark=lambda name: next(it).record(stream))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+                for i, name in enumerate(BWD_STAGES)}
+    return (t1 - t0) * 1e3 / steps, stage_ms
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +163,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e8m0", action="store_true",
                     help="skip the timing of the power-of-two (E8M0) scale variant")
+    ap.add_argument("--no-backward", action="store_true", help="skip the timing of the backward")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -232,6 +253,34 @@ def main():
         "context": "pages: 2.788M H800 GPU-hours for the whole V3 training run; "
                    "180K H800 GPU-hours per trillion training tokens (not comparable)",
     }
+    if not args.no_backward:
+        Wt = W.transposed()
+        layer.forward(x, wg, b, W, train=True)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(cfg.seed * 7 + 3)
+        dout = torch.randn(cfg.T, cfg.d, generator=g, device="cuda").to(torch.bfloat16)
+        for _ in range(max(1, args.warmup // 2)):
+            layer.backward(dout, Wt)
+        msb, stb = timed_backward(layer, dout, Wt, args.steps)
+        log(f"backward: {msb:.3f} ms/step; stages " + ", ".join(f"{k} {v:.3f}" for k, v in stb.items()))
+        f_w2 = rows * 2 * cfg.d * cfg.f          # each of Dgrad W2 and Wgrad W2
+        f_w13 = rows * 2 * (2 * cfg.f) * cfg.d   # each of Dgrad W13 and Wgrad W13
+        dgrad_ms = stb["dgrad_w2"] + stb["dgrad_w13"]
+        wgrad_ms = stb["wgrad_w2"] + stb["wgrad_w13"]
+        result["backward"] = {
+            "ms_per_step": msb, "stages_ms": stb, "tokens_per_s": cfg.T / (msb * 1e-3),
+            "dgrad_tflops": (f_w2 + f_w13) / (dgrad_ms * 1e-3) / 1e12,
+            "wgrad_tflops": (f_w2 + f_w13) / (wgrad_ms * 1e-3) / 1e12,
+            "wgrad_w13_tflops": f_w13 / (stb["wgrad_w13"] * 1e-3) / 1e12,
+            "weight_grad_bytes_written": 3 * (cfg.E + 1) * cfg.d * cfg.f * 4,
+            "note": "dgrad_w13 includes the token-gradient gather; Wgrad writes FP32 gradients of "
+                    "all experts",
+        }
+        del Wt, dout
+        layer.__dict__.update({k: None for k in ("gu", "gus", "dy", "dyq", "dys", "dh", "dgu", "dgus",
+                                                 "dgu_t", "dgu_ts", "h_t", "h_ts", "dy_t", "dy_ts", "x_t",
+                                                 "x_ts", "dx_rows", "dx", "dw13", "dw2")})
+        torch.cuda.empty_cache()
     if not args.no_e8m0:
         del W, layer
         torch.cuda.empty_cache()
