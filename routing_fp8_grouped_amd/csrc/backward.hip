@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void regroup_128x1_kernel(
     const int32_t* __restrict__ row_src, const int32_t* __restrict__ offsets, int n_groups, int C,
     int Kp, uint8_t* __restrict__ out, float* __restrict__ out_s) {
   __shared__ int pb[BW_MAX_GROUPS + 1];
-  __shared__ float tile[128][129];
+  __shared__ __attribute__((aligned(16))) float tile[128][129];   // values, then [column][row] codes
   __shared__ float colmax[2][128];
   const int tid = threadIdx.x, cb = blockIdx.x, blk = blockIdx.y;
   if (tid < 64) padded_block_prefix(offsets, n_groups, pb, tid);
@@ -193,24 +193,37 @@ __global__ __launch_bounds__(256) void regroup_128x1_kernel(
     for (int i = 0; i < 64; ++i) tile[r][half * 64 + i] = v[i];
   }
   __syncthreads();
+  // column phase: thread (c, part) holds rows [64 part, 64 part + 64) of column c
   const int c = tid & 127, part = tid >> 7;
+  float w[64];
   float amax = 0.0f;
-  for (int r = part * 64; r < part * 64 + 64; ++r) amax = fmaxf(amax, fabsf(tile[r][c]));
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    w[i] = tile[part * 64 + i][c];
+    amax = fmaxf(amax, fabsf(w[i]));
+  }
   colmax[part][c] = amax;
   __syncthreads();
   const float s = scale_from_amax_pow2(fmaxf(colmax[0][c], colmax[1][c]));
-  uint8_t* dst = out + (size_t)(cb * 128 + c) * Kp + (size_t)blk * 128 + part * 64;
+  const float inv = 1.0f / s;   // exact: s is a power of two
+  uint32_t pk[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    pk[j] = f32x4_to_e4m3(w[4 * j] * inv, w[4 * j + 1] * inv, w[4 * j + 2] * inv, w[4 * j + 3] * inv);
+  if (part == 0) out_s[(size_t)blk * C + cb * 128 + c] = s;
+  __syncthreads();   // every read of tile is done: its memory now holds the codes
+  uint8_t(*tq)[144] = reinterpret_cast<uint8_t(*)[144]>(&tile[0][0]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint4*>(&tq[c][part * 64 + i * 16]) = make_uint4(pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]);
+  __syncthreads();
+  // full 128-byte output rows: 8 lanes per row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = part * 64 + i * 16;
-    uint32_t u[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      u[j] = f32x4_to_e4m3(tile[r + 4 * j][c] / s, tile[r + 4 * j + 1][c] / s, tile[r + 4 * j + 2][c] / s,
-                           tile[r + 4 * j + 3][c] / s);
-    *reinterpret_cast<uint4*>(dst + i * 16) = make_uint4(u[0], u[1], u[2], u[3]);
+    const int cc = (tid >> 3) + 32 * i, ch = tid & 7;
+    *reinterpret_cast<uint4*>(out + (size_t)(cb * 128 + cc) * Kp + (size_t)blk * 128 + ch * 16) =
+        *reinterpret_cast<const uint4*>(&tq[cc][ch * 16]);
   }
-  if (part == 0) out_s[(size_t)blk * C + cb * 128 + c] = s;
 }
 
 // ---- SwiGLU backward ----
@@ -234,136 +247,150 @@ __device__ __forceinline__ SwigluVals swiglu_bwd_vals(float g, float u, float dh
   return r;
 }
 
-__global__ __launch_bounds__(256) void swiglu_backward_kernel(
+// Four threads (4r .. 4r+3, one wave) own row r of the tile, 32 columns each:
+// h, dG, dU are evaluated once (FP64) and kept in registers; a row's amax is
+// in-thread plus two shuffles; a column's amax goes through an LDS table, one
+// quantity at a time; the transposed codes are staged in LDS.  Division by a
+// power-of-two scale is a multiplication by its exact inverse.
+constexpr int SWB_THREADS = 512;
+
+__global__ __launch_bounds__(SWB_THREADS) void swiglu_backward_kernel(
     const uint8_t* __restrict__ guq, const float* __restrict__ gus, const uint16_t* __restrict__ dh,
     const int32_t* __restrict__ offsets, int n_groups, int f, int Kp, uint8_t* __restrict__ dguq,
     float* __restrict__ dgus, uint8_t* __restrict__ dgut, float* __restrict__ dguts,
     uint8_t* __restrict__ ht, float* __restrict__ hts) {
   __shared__ int pb[BW_MAX_GROUPS + 1];
-  __shared__ uint8_t gq[128][128];
-  __shared__ uint8_t uq[128][128];
-  __shared__ uint16_t dhs[128][130];
-  __shared__ float gsc[128], usc[128];
-  __shared__ uint32_t rmax_g[128], rmax_u[128];   // FP32 bits of non-negative row amax
-  __shared__ float cmax[3][2][128];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[2][128][128];
+  __shared__ __attribute__((aligned(16))) float red[128][129];   // values, then [column][row] codes
+  __shared__ float part_max[4][128];
   const int tid = threadIdx.x, cb = blockIdx.x, blk = blockIdx.y;
   if (tid < 64) padded_block_prefix(offsets, n_groups, pb, tid);
-  if (tid < 128) {
-    rmax_g[tid] = 0u;
-    rmax_u[tid] = 0u;
-  }
   __syncthreads();
   if (blk >= pb[n_groups]) return;   // uniform
   const int e = block_group(pb, n_groups, blk);
   const int row0 = offsets[e] + (blk - pb[e]) * 128;
   const int nrows = min(128, offsets[e + 1] - row0);
   const int nsc = 2 * f / 128;
+  const int r = tid >> 2, qt = tid & 3, col0 = qt * 32;
+  const bool valid = r < nrows;
+  const size_t rowi = (size_t)(row0 + r);
+  float vh[32], vg[32], vu[32];
   {
-    const int r = tid >> 1, half = tid & 1;
-    if (r < nrows) {
-      const size_t rowi = (size_t)(row0 + r);
-      const uint8_t* pg = guq + rowi * 2 * f + cb * 128 + half * 64;
-      const uint8_t* pu = pg + f;
+    uint32_t gw[8], uw[8], dw[16];
+    if (valid) {
+      const uint8_t* pg = guq + rowi * 2 * f + cb * 128 + col0;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 a = *reinterpret_cast<const uint4*>(pg + i * 16);
+        const uint4 b = *reinterpret_cast<const uint4*>(pg + f + i * 16);
+        gw[4 * i] = a.x; gw[4 * i + 1] = a.y; gw[4 * i + 2] = a.z; gw[4 * i + 3] = a.w;
+        uw[4 * i] = b.x; uw[4 * i + 1] = b.y; uw[4 * i + 2] = b.z; uw[4 * i + 3] = b.w;
+      }
+      const uint16_t* pd = dh + rowi * f + cb * 128 + col0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4*>(&gq[r][half * 64 + i * 16]) = *reinterpret_cast<const uint4*>(pg + i * 16);
-        *reinterpret_cast<uint4*>(&uq[r][half * 64 + i * 16]) = *reinterpret_cast<const uint4*>(pu + i * 16);
-      }
-      const uint16_t* pd = dh + rowi * f + cb * 128 + half * 64;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
         const uint4 q = *reinterpret_cast<const uint4*>(pd + i * 8);
-        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dhs[r][half * 64 + i * 8 + 2 * j] = (uint16_t)(u[j] & 0xFFFFu);
-          dhs[r][half * 64 + i * 8 + 2 * j + 1] = (uint16_t)(u[j] >> 16);
-        }
-      }
-      if (half == 0) {
-        gsc[r] = gus[rowi * nsc + cb];
-        usc[r] = gus[rowi * nsc + f / 128 + cb];
+        dw[4 * i] = q.x; dw[4 * i + 1] = q.y; dw[4 * i + 2] = q.z; dw[4 * i + 3] = q.w;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        gq[r][half * 64 + i] = 0;
-        uq[r][half * 64 + i] = 0;
-        dhs[r][half * 64 + i] = 0;
-      }
-      if (half == 0) gsc[r] = usc[r] = 0.0f;
-    }
-  }
-  __syncthreads();
-  // column layout: thread -> column c, rows part*64 .. +63
-  const int c = tid & 127, part = tid >> 7;
-  float mh = 0.0f, mg = 0.0f, mu = 0.0f;
-  for (int r = part * 64; r < part * 64 + 64; ++r) {
-    const SwigluVals v = swiglu_bwd_vals(e4m3_to_f32(gq[r][c]) * gsc[r], e4m3_to_f32(uq[r][c]) * usc[r],
-                                         bf16_to_f32(dhs[r][c]));
-    mh = fmaxf(mh, fabsf(v.h));
-    mg = fmaxf(mg, fabsf(v.dg));
-    mu = fmaxf(mu, fabsf(v.du));
-    atomicMax(&rmax_g[r], __float_as_uint(fabsf(v.dg)));
-    atomicMax(&rmax_u[r], __float_as_uint(fabsf(v.du)));
-  }
-  cmax[0][part][c] = mh;
-  cmax[1][part][c] = mg;
-  cmax[2][part][c] = mu;
-  __syncthreads();
-  const float sh = scale_from_amax_pow2(fmaxf(cmax[0][0][c], cmax[0][1][c]));
-  const float sg = scale_from_amax_pow2(fmaxf(cmax[1][0][c], cmax[1][1][c]));
-  const float su = scale_from_amax_pow2(fmaxf(cmax[2][0][c], cmax[2][1][c]));
-  uint8_t* oh = ht + (size_t)(cb * 128 + c) * Kp + (size_t)blk * 128 + part * 64;
-  uint8_t* og = dgut + (size_t)(cb * 128 + c) * Kp + (size_t)blk * 128 + part * 64;
-  uint8_t* ou = dgut + (size_t)(f + cb * 128 + c) * Kp + (size_t)blk * 128 + part * 64;
-#pragma unroll 1
-  for (int i = 0; i < 4; ++i) {
-    uint32_t wh[4], wg[4], wu[4];
+      for (int i = 0; i < 8; ++i) gw[i] = uw[i] = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float vh[4], vg[4], vu[4];
+      for (int i = 0; i < 16; ++i) dw[i] = 0u;
+    }
+    const float gs = valid ? gus[rowi * nsc + cb] : 0.0f;
+    const float us = valid ? gus[rowi * nsc + f / 128 + cb] : 0.0f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = part * 64 + i * 16 + j * 4 + q;
-        const SwigluVals v = swiglu_bwd_vals(e4m3_to_f32(gq[r][c]) * gsc[r], e4m3_to_f32(uq[r][c]) * usc[r],
-                                             bf16_to_f32(dhs[r][c]));
-        vh[q] = v.h;
-        vg[q] = v.dg;
-        vu[q] = v.du;
-        // row-major copy with the row's power-of-two scale
-        stage[0][r][c] = (uint8_t)(f32x2_to_e4m3(v.dg / scale_from_amax_pow2(__uint_as_float(rmax_g[r])), 0.0f) & 0xFFu);
-        stage[1][r][c] = (uint8_t)(f32x2_to_e4m3(v.du / scale_from_amax_pow2(__uint_as_float(rmax_u[r])), 0.0f) & 0xFFu);
+    for (int i = 0; i < 32; ++i) {
+      const float g = e4m3_to_f32((gw[i >> 2] >> (8 * (i & 3))) & 0xFFu) * gs;
+      const float u = e4m3_to_f32((uw[i >> 2] >> (8 * (i & 3))) & 0xFFu) * us;
+      const float d = bf16_to_f32((uint16_t)(dw[i >> 1] >> (16 * (i & 1))));
+      const SwigluVals v = swiglu_bwd_vals(g, u, d);
+      vh[i] = v.h;
+      vg[i] = v.dg;
+      vu[i] = v.du;
+      // materialise the three FP32 results here, so that no FP64 temporaries
+      // are carried into the quantisation passes
+      asm volatile("" : "+v"(vh[i]), "+v"(vg[i]), "+v"(vu[i]));
+    }
+  }
+  // ---- [dG, dU] in row order: 1x128 tiles, power-of-two scales ----
+  {
+    float mg = 0.0f, mu = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      mg = fmaxf(mg, fabsf(vg[i]));
+      mu = fmaxf(mu, fabsf(vu[i]));
+    }
+    mg = fmaxf(mg, __shfl_xor(mg, 1));
+    mu = fmaxf(mu, __shfl_xor(mu, 1));
+    mg = fmaxf(mg, __shfl_xor(mg, 2));
+    mu = fmaxf(mu, __shfl_xor(mu, 2));
+    const float sg = scale_from_amax_pow2(mg), su = scale_from_amax_pow2(mu);
+    const float ig = 1.0f / sg, iu = 1.0f / su;
+    if (valid) {
+      uint8_t* og = dguq + rowi * 2 * f + cb * 128 + col0;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        uint32_t a[4], b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 16 * i + 4 * j;
+          a[j] = f32x4_to_e4m3(vg[c] * ig, vg[c + 1] * ig, vg[c + 2] * ig, vg[c + 3] * ig);
+          b[j] = f32x4_to_e4m3(vu[c] * iu, vu[c + 1] * iu, vu[c + 2] * iu, vu[c + 3] * iu);
+        }
+        *reinterpret_cast<uint4*>(og + i * 16) = make_uint4(a[0], a[1], a[2], a[3]);
+        *reinterpret_cast<uint4*>(og + f + i * 16) = make_uint4(b[0], b[1], b[2], b[3]);
       }
-      wh[j] = f32x4_to_e4m3(vh[0] / sh, vh[1] / sh, vh[2] / sh, vh[3] / sh);
-      wg[j] = f32x4_to_e4m3(vg[0] / sg, vg[1] / sg, vg[2] / sg, vg[3] / sg);
-      wu[j] = f32x4_to_e4m3(vu[0] / su, vu[1] / su, vu[2] / su, vu[3] / su);
-    }
-    *reinterpret_cast<uint4*>(oh + i * 16) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    *reinterpret_cast<uint4*>(og + i * 16) = make_uint4(wg[0], wg[1], wg[2], wg[3]);
-    *reinterpret_cast<uint4*>(ou + i * 16) = make_uint4(wu[0], wu[1], wu[2], wu[3]);
-  }
-  if (part == 0) {
-    hts[(size_t)blk * f + cb * 128 + c] = sh;
-    dguts[(size_t)blk * 2 * f + cb * 128 + c] = sg;
-    dguts[(size_t)blk * 2 * f + f + cb * 128 + c] = su;
-  }
-  __syncthreads();
-  // row-major [dG, dU] codes and scales of the valid rows
-  for (int idx = tid; idx < 128 * 16; idx += 256) {
-    const int r = idx >> 4, q = idx & 15, which = q >> 3, c16 = q & 7;
-    if (r < nrows) {
-      const size_t rowi = (size_t)(row0 + r);
-      *reinterpret_cast<uint4*>(dguq + rowi * 2 * f + which * f + cb * 128 + c16 * 16) =
-          *reinterpret_cast<const uint4*>(&stage[which][r][c16 * 16]);
+      if (qt == 0) {
+        dgus[rowi * nsc + cb] = sg;
+        dgus[rowi * nsc + f / 128 + cb] = su;
+      }
     }
   }
-  if (tid < 128 && tid < nrows) {
-    const size_t rowi = (size_t)(row0 + tid);
-    dgus[rowi * nsc + cb] = scale_from_amax_pow2(__uint_as_float(rmax_g[tid]));
-    dgus[rowi * nsc + f / 128 + cb] = scale_from_amax_pow2(__uint_as_float(rmax_u[tid]));
-  }
+  // ---- K-major 128x1 copies: h -> ht, dG -> dgut rows [0, f), dU -> dgut rows [f, 2f) ----
+  uint8_t(*tq)[144] = reinterpret_cast<uint8_t(*)[144]>(&red[0][0]);   // aliases red
+  auto pass = [&](const float(&v)[32], int q) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) red[r][col0 + i] = v[i];
+    __syncthreads();
+    // column phase: thread (c, rq) holds rows [32 rq, 32 rq + 32) of column c
+    const int c = tid & 127, rq = tid >> 7;
+    float w[32];
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      w[j] = red[rq * 32 + j][c];
+      m = fmaxf(m, fabsf(w[j]));
+    }
+    part_max[rq][c] = m;
+    __syncthreads();   // every read of red is done: its memory now holds the codes
+    m = fmaxf(fmaxf(part_max[0][c], part_max[1][c]), fmaxf(part_max[2][c], part_max[3][c]));
+    const float sc = scale_from_amax_pow2(m);
+    const float inv = 1.0f / sc;   // exact: sc is a power of two
+    if (rq == 0) {
+      if (q == 0) hts[(size_t)blk * f + cb * 128 + c] = sc;
+      else dguts[(size_t)blk * 2 * f + (q - 1) * f + cb * 128 + c] = sc;
+    }
+    uint32_t pk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      pk[j] = f32x4_to_e4m3(w[4 * j] * inv, w[4 * j + 1] * inv, w[4 * j + 2] * inv, w[4 * j + 3] * inv);
+    *reinterpret_cast<uint4*>(&tq[c][rq * 32]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<uint4*>(&tq[c][rq * 32 + 16]) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    __syncthreads();
+    // full 128-byte output rows: 8 lanes per row
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int cc = (tid >> 3) + 64 * i, ch = tid & 7;
+      uint8_t* dst = q == 0 ? ht + (size_t)(cb * 128 + cc) * Kp
+                            : dgut + (size_t)((q - 1) * f + cb * 128 + cc) * Kp;
+      *reinterpret_cast<uint4*>(dst + (size_t)blk * 128 + ch * 16) = *reinterpret_cast<const uint4*>(&tq[cc][ch * 16]);
+    }
+    __syncthreads();   // before the next pass overwrites red
+  };
+  pass(vh, 0);
+  pass(vg, 1);
+  pass(vu, 2);
 }
 
 hipError_t launch_transpose_blocks(const uint8_t* w, const float* ws, int G, int N, int K, uint8_t* wt,
@@ -402,7 +429,7 @@ hipError_t launch_swiglu_backward(const uint8_t* guq, const float* gus, const ui
                                   uint8_t* dguq, float* dgus, uint8_t* dgut, float* dguts, uint8_t* ht,
                                   float* hts, hipStream_t stream) {
   const dim3 grid(f / 128, wgrad_blocks_bound(total_rows, n_groups));
-  hipLaunchKernelGGL(swiglu_backward_kernel, grid, dim3(256), 0, stream, guq, gus, dh, offsets, n_groups, f,
+  hipLaunchKernelGGL(swiglu_backward_kernel, grid, dim3(SWB_THREADS), 0, stream, guq, gus, dh, offsets, n_groups, f,
                      Kp, dguq, dgus, dgut, dguts, ht, hts);
   return hipGetLastError();
 }
