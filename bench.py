@@ -159,7 +159,7 @@ def main():
     ap.add_argument("--workload", default="uniform_16k", choices=sorted(configs.CONFIGS))
     ap.add_argument("--dispatch", action="store_true",
                     help="copy the FP8 rows into grouped order instead of gathering in the GEMM")
-    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e8m0", action="store_true",
                     help="skip the timing of the power-of-two (E8M0) scale variant")

@@ -176,7 +176,9 @@ __device__ __forceinline__ void build_sources(const GemmArgs& p, const Tile& t, 
     const int c = pc ^ swz(r);
     int row = p.row_src ? table[r] : tile_row(p, t, r);
     row = min(max(row, 0), p.a_rows - 1);
-    srcw[i * 64 + lane] = (uint32_t)row * (uint32_t)p.K + c * 16;
+    // rows past the end of a partial tile are not loaded (their LDS rows are
+    // multiplied but never stored); an odd offset marks them
+    srcw[i * 64 + lane] = r < t.rows_valid ? (uint32_t)row * (uint32_t)p.K + c * 16 : 1u;
     int wr = weight_row<SWIGLU>(p, t.n, r);
     if (wr >= p.N) wr = 0;   // padding rows of a partial tile: any valid row, never stored
     srcw[(4 + i) * 64 + lane] = (uint32_t)wr * (uint32_t)p.K + c * 16;
@@ -203,7 +205,10 @@ __device__ __forceinline__ void issue_stage(const GemmArgs& p, const uint8_t* bb
   const uint8_t* a = p.a + (size_t)kb * BK;
   const uint8_t* b = bbase + (size_t)kb * BK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(a, srcw[i * 64 + lane], base + (wave * 4 + i) * 1024);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t src = srcw[i * 64 + lane];
+    if (!(src & 1u)) dma16(a, src, base + (wave * 4 + i) * 1024);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) dma16(b, srcw[(4 + i) * 64 + lane], base + ST_A + (wave * 4 + i) * 1024);
   if (wave < 4) dma4(p.as + kb, srcw[8 * 64 + lane], base + ST_A + ST_B + wave * 256);
