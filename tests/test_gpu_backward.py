@@ -337,3 +337,120 @@ def test_tiny_layer_backward():
     log(f"  relative L2 max: dH rows {worst['dh']:.2e}, dX rows {worst['dx_rows']:.2e}, "
         f"dW {worst['dw']:.2e}; token dX end to end {e2e:.2e}")
     assert e2e <= TOL
+
+
+def _padded_blocks(off):
+    nb = -(-np.diff(np.asarray(off, np.int64)) // 128)
+    return np.concatenate([[0], np.cumsum(nb)]).astype(np.int64)
+
+
+def test_v3_backward_sampled():
+    """The backward at the full 16k-token V3 shape, in the configuration the
+    bench times, checked on samples the oracle computes one by one: the rows of
+    two tokens through every row-local stage, one 128-row block of a routed
+    and of the shared expert through the regrouping and the transposed SwiGLU
+    outputs, and 32 x 32 weight-gradient elements of both experts."""
+    cfg = configs.get("uniform_16k")
+    T, k, E, d, f = cfg.T, cfg.k, cfg.E, cfg.d, cfg.f
+    log(f"layer backward {cfg.name}: T={T} d={d} E={E} f={f}")
+    x, wg, b = inputs.host_inputs(cfg)
+    W = device_weights(cfg)
+    Wt = W.transposed()
+    L = moe.MoELayer(T, d, E, cfg.G, cfg.M, k, f, cfg.route_scale)
+    L.forward(x.to(DEV), wg.to(DEV), b.to(DEV), W, train=True)
+    gen = torch.Generator(device=DEV).manual_seed(7)
+    dout = torch.randn(T, d, generator=gen, device=DEV).to(torch.bfloat16)
+    dx, dw13, dw2, dgate = L.backward(dout, Wt)
+    torch.cuda.synchronize()
+    log("  forward + backward done on the GPU")
+    pos, off = to_np(L.pos), to_np(L.offsets)
+    rt = to_np(L.row_token)
+    rng = np.random.default_rng(8)
+    tok = np.sort(rng.choice(T, 2, replace=False))
+    ns = len(tok)
+    rows = np.concatenate([pos[tok].reshape(-1), T * k + tok])
+    R = torch.from_numpy(rows.astype(np.int64)).to(DEV)
+    pos_l = np.arange(ns * k).reshape(ns, k)
+    dout_s = dout[torch.from_numpy(tok).to(DEV)].float().cpu().numpy()
+    # combine backward: dY rows bit-exact, gate gradients within the FP32 sum's bound
+    ys = to_np(L.y[R])
+    rdy, rdw = ob.combine_backward(dout_s, ys, to_np(L.w)[tok], pos_l, ns, k)
+    assert np.array_equal(to_np(L.dy[R]), rdy)
+    # FP32 dot products of length d: at most ~40 sequential roundings per element
+    dw_bound = 40 * 2.0 ** -24 * np.einsum("td,tkd->tk", np.abs(dout_s), np.abs(ys[pos_l]))
+    assert np.all(np.abs(to_np(dgate)[tok] - rdw) <= dw_bound)
+    dyq, dys = oq.quant_1x128(rdy, "pow2")
+    assert np.array_equal(to_np(L.dyq[R]), dyq) and np.array_equal(to_np(L.dys[R]), dys)
+    # row-local stages on the GPU's own inputs to each stage
+    experts = np.searchsorted(off, rows, side="right") - 1
+    oe = OracleExperts(cfg)
+    oe.prepare(sorted(set(experts.tolist())))
+    log(f"  oracle: {len(set(experts.tolist()))} experts for tokens {tok.tolist()}")
+    gdh, gdgu, gdgus, gdx = (to_np(getattr(L, n)[R]) for n in ("dh", "dgu", "dgus", "dx_rows"))
+    gu, gus = to_np(L.gu[R]), to_np(L.gus[R])
+    worst_dh = worst_dx = 0.0
+    n_flip = 0
+    for i, e in enumerate(experts):
+        w13q, w13s, w2q, w2s = oe(int(e))
+        r = slice(i, i + 1)
+        rdh = fp8.bf16_round(fp8.f32(olayer.blocked_gemm(dyq[r], dys[r], w2q.T.copy(), w2s.T.copy())))
+        gv = fp8.f32(oq.dequant_1x128(gu[r], gus[r]))
+        _, dg, du = (fp8.f32(v) for v in ob.swiglu_backward(gv[:, :f], gv[:, f:], gdh[r]))
+        rq, rs = oq.quant_1x128(np.concatenate([dg, du], axis=1), "pow2")
+        n_flip += _close_codes(gdgu[r], rq, "dgu")
+        assert np.array_equal(gdgus[r], rs)
+        rdx = fp8.bf16_round(fp8.f32(olayer.blocked_gemm(gdgu[r], gdgus[r], w13q.T.copy(), w13s.T.copy())))
+        worst_dh = max(worst_dh, float(rel_l2_rows(gdh[r], rdh).max()))
+        worst_dx = max(worst_dx, float(rel_l2_rows(gdx[r], rdx).max()))
+    assert worst_dh <= TOL and worst_dx <= TOL, (worst_dh, worst_dx)
+    # token gradient: the float64 sum of the GPU's rows, rounded once
+    rdx_tok = ob.token_grad(gdx, pos_l, ns, k)
+    got_tok = to_np(dx[torch.from_numpy(tok).to(DEV)])
+    assert np.array_equal(got_tok, rdx_tok) or rel_l2_rows(got_tok, rdx_tok).max() <= 2.0 ** -7
+    # one 128-row block of a routed expert (its last, usually partial) and of the
+    # shared expert: regrouped dY and X, transposed h and [dG, dU]
+    pb = _padded_blocks(off)
+    routed = int(rng.choice(np.nonzero(np.diff(off[:E + 1]))[0]))
+    blocks = [(routed, int(pb[routed + 1] - pb[routed] - 1)), (E, int(rng.integers(0, pb[E + 1] - pb[E])))]
+    xq, xs = L.xq, L.xs
+    for e, blk in blocks:
+        r0 = int(off[e]) + 128 * blk
+        r1 = min(r0 + 128, int(off[e + 1]))
+        c = int(pb[e]) + blk
+        cols = slice(128 * c, 128 * c + 128)
+        src = torch.from_numpy(rt[r0:r1].astype(np.int64)).to(DEV)
+        xv = fp8.f32(oq.dequant_1x128(to_np(xq[src]), to_np(xs[src])))
+        gb = to_np(L.gu[r0:r1]), to_np(L.gus[r0:r1])
+        gv = fp8.f32(oq.dequant_1x128(*gb))
+        h, dg, du = (fp8.f32(v) for v in ob.swiglu_backward(gv[:, :f], gv[:, f:], to_np(L.dh[r0:r1])))
+        for name, vals, exact in (("dy_t", to_np(L.dy[r0:r1]), True), ("x_t", xv, True),
+                                  ("h_t", h, False), ("dgu_t", np.concatenate([dg, du], axis=1), False)):
+            q, s_ = ob.quant_128x1(vals)
+            gq = to_np(getattr(L, name)[:, cols])
+            gs = to_np(getattr(L, name + "s")[c])
+            if exact:
+                assert np.array_equal(gq, q.T), (name, e, blk)
+            else:
+                n_flip += _close_codes(gq, q.T, name)
+            assert np.array_equal(gs, s_[0]), (name, e, blk)
+    # weight gradients: 32 x 32 elements of each of the two experts, on the GPU's operands
+    worst_dw = 0.0
+    for e, _ in blocks:
+        sl = slice(128 * int(pb[e]), 128 * int(pb[e + 1]))
+        ss = slice(int(pb[e]), int(pb[e + 1]))
+        for got_all, (a, b_), (M, N) in ((dw2, ("dy_t", "h_t"), (d, f)), (dw13, ("dgu_t", "x_t"), (2 * f, d))):
+            mi = np.sort(rng.choice(M, 32, replace=False))
+            ni = np.sort(rng.choice(N, 32, replace=False))
+            MI, NI = (torch.from_numpy(v.astype(np.int64)).to(DEV) for v in (mi, ni))
+            got = to_np(got_all[e][MI][:, NI])
+            aq = to_np(getattr(L, a)[MI][:, sl])
+            as_ = to_np(getattr(L, a + "s")[ss][:, MI]).T.copy()
+            bq = to_np(getattr(L, b_)[NI][:, sl])
+            bs = to_np(getattr(L, b_ + "s")[ss][:, NI]).T.copy()
+            exact = ob.gemm_rows_scaled(aq, as_, bq, bs)
+            err = np.abs(got - exact)
+            bound = wgrad_bound(aq, as_, bq, bs, exact)
+            assert np.all(err <= bound), (e, a, float((err / np.maximum(bound, 1e-300)).max()))
+            worst_dw = max(worst_dw, float(np.linalg.norm(got - exact) / np.linalg.norm(exact)))
+    log(f"  relative L2 max: dH rows {worst_dh:.2e}, dX rows {worst_dx:.2e}, dW samples {worst_dw:.2e}; "
+        f"one-step code differences {n_flip}; blocks checked {blocks}")
