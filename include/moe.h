@@ -85,6 +85,26 @@ moe_status moe_route(const uint16_t* x, const uint16_t* wg, const float* bias,
                      int T, int d, moe_route_params p,
                      int32_t* idx, float* w, void* stream);
 
+/* Bytes of device workspace moe_route_ws needs for T tokens and E experts
+ * (FP32 logits [T, E], rounded up to 256), or 0 where it uses moe_route's
+ * single kernel (T above 8192, or T, E out of range). */
+size_t moe_route_workspace_bytes(int T, int E);
+
+/* moe_route_ws — moe_route with a caller-owned workspace, the same results
+ * bit for bit.  For small batches one workgroup per 64 tokens would stream
+ * all E centroid rows alone; here the logits are computed by workgroups of
+ * (16 tokens, 32 experts) for T <= 1024 or (64 tokens, 64 experts) for
+ * T <= 8192, each over all of d in the same order of arithmetic, written to
+ * the workspace, and a second kernel selects.
+ *   workspace        device memory of at least moe_route_workspace_bytes(T, E)
+ *                    bytes, 4-byte aligned (may be NULL when that is 0);
+ *                    overwritten; calls that share it must not overlap
+ * Errors as moe_route, and MOE_ERR_WORKSPACE for a missing, misaligned or
+ * short workspace. */
+moe_status moe_route_ws(const uint16_t* x, const uint16_t* wg, const float* bias,
+                        int T, int d, moe_route_params p, int32_t* idx, float* w,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* fp8_quant_1x128 — activation quantisation (summary page section 6 (a), (d)).
  *   x      [rows, cols] BF16, cols % 128 == 0
  *   q      [rows, cols] E4M3 out

@@ -15,7 +15,7 @@ import torch
 from . import _lib
 from ._lib import MoEError, RouteParams  # noqa: F401
 
-__all__ = ["moe_route", "fp8_quant_1x128", "fp8_quant_128x128", "moe_permute_workspace_bytes",
+__all__ = ["moe_route", "moe_route_workspace_bytes", "fp8_quant_1x128", "fp8_quant_128x128", "moe_permute_workspace_bytes",
            "moe_permute", "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up", "grouped_gemm_fp8_down",
            "moe_combine", "moe_bias_update", "fp8_quant_1x128_pow2", "fp8_quant_128x128_pow2",
            "grouped_gemm_fp8_up_e8m0", "grouped_gemm_fp8_down_e8m0", "grouped_gemm_fp8_up_train",
@@ -44,15 +44,28 @@ def _dev(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def moe_route(x, wg, bias, n_groups, topk_groups, topk, route_scale, idx, w, stream=None):
-    """Router: idx [T, k] int32 (ascending expert ids), w [T, k] float32."""
+def moe_route_workspace_bytes(T, E):
+    return int(_lib.load().moe_route_workspace_bytes(T, E))
+
+
+def moe_route(x, wg, bias, n_groups, topk_groups, topk, route_scale, idx, w, stream=None, workspace=None):
+    """Router: idx [T, k] int32 (ascending expert ids), w [T, k] float32.
+    With ``workspace`` (a uint8 device tensor of moe_route_workspace_bytes(T, E)
+    bytes) it runs moe_route_ws: the same results, the logits spread over more
+    workgroups for small batches."""
     _dev(x, torch.bfloat16, "x"); _dev(wg, torch.bfloat16, "wg"); _dev(bias, torch.float32, "bias")
     _dev(idx, torch.int32, "idx"); _dev(w, torch.float32, "w")
     T, d = x.shape
     p = RouteParams(wg.shape[0], n_groups, topk_groups, topk, route_scale)
     lib = _lib.load()
-    _lib.check("moe_route", lib.moe_route(_ptr(x), _ptr(wg), _ptr(bias), T, d, p, _ptr(idx), _ptr(w),
-                                          _stream(stream)))
+    if workspace is None:
+        _lib.check("moe_route", lib.moe_route(_ptr(x), _ptr(wg), _ptr(bias), T, d, p, _ptr(idx), _ptr(w),
+                                              _stream(stream)))
+    else:
+        _dev(workspace, torch.uint8, "workspace")
+        _lib.check("moe_route_ws", lib.moe_route_ws(_ptr(x), _ptr(wg), _ptr(bias), T, d, p, _ptr(idx),
+                                                    _ptr(w), _ptr(workspace), workspace.numel(),
+                                                    _stream(stream)))
 
 
 def _quant_1x128(name, x, q, scale, stream):
@@ -351,6 +364,7 @@ class MoELayer:
         self.pos = torch.empty(T, topk, dtype=torch.int32, **dev)
         self.row_token = torch.empty(rows, dtype=torch.int32, **dev)
         self.ws = torch.empty(max(16, moe_permute_workspace_bytes(T, topk, E)), dtype=torch.uint8, **dev)
+        self.route_ws = torch.empty(max(16, moe_route_workspace_bytes(T, E)), dtype=torch.uint8, **dev)
         self.xq_perm = torch.empty(rows, d, dtype=torch.uint8, **dev) if dispatch else None
         self.xs_perm = torch.empty(rows, d // 128, dtype=torch.float32, **dev) if dispatch else None
         self.h = torch.empty(rows, f, dtype=torch.uint8, **dev)
@@ -365,7 +379,7 @@ class MoELayer:
         ``backward`` (FP32-scale method only)."""
         mark = mark or (lambda name: None)
         moe_route(x, wg, bias, self.n_groups, self.topk_groups, self.k, self.route_scale,
-                  self.idx, self.w, stream)
+                  self.idx, self.w, stream, workspace=self.route_ws)
         mark("route")
         (fp8_quant_1x128_pow2 if self.pow2 else fp8_quant_1x128)(x, self.xq, self.xs, stream)
         mark("quant")

@@ -37,6 +37,8 @@ SZ = ctypes.c_size_t
 
 SIGNATURES = {
     "moe_route": (I, [P, P, P, I, I, RouteParams, P, P, P]),
+    "moe_route_workspace_bytes": (SZ, [I, I]),
+    "moe_route_ws": (I, [P, P, P, I, I, RouteParams, P, P, P, SZ, P]),
     "fp8_quant_1x128": (I, [P, I, I, P, P, P]),
     "fp8_quant_128x128": (I, [P, I, I, P, P, P]),
     "moe_permute_workspace_bytes": (SZ, [I, I, I]),

@@ -104,6 +104,7 @@ moe_status moe_route(const uint16_t* x, const uint16_t* wg, const float* bias, i
   REQUIRE(d >= 128 && d % 128 == 0, "d=%d must be a positive multiple of 128", d);
   if (T == 0) return MOE_OK;
   REQUIRE(T <= INT32_MAX / p.topk, "T*k overflows int32");
+  REQUIRE((uint64_t)T * (uint64_t)d * 2u <= 0xFFFFFFFFull, "x of T=%d rows x d=%d exceeds 4 GiB", T, d);
   REQUIRE_PTR(x);
   REQUIRE_PTR(wg);
   REQUIRE_ALIGNED4_OR_NULL(bias);
@@ -113,6 +114,40 @@ moe_status moe_route(const uint16_t* x, const uint16_t* wg, const float* bias, i
                                       p.topk, p.route_scale, idx, w,
                                       static_cast<hipStream_t>(stream)),
                     "moe_route launch");
+}
+
+size_t moe_route_workspace_bytes(int T, int E) {
+  if (E < 1 || E > 256) return 0;
+  return moe::route_workspace_bytes(T, E);
+}
+
+moe_status moe_route_ws(const uint16_t* x, const uint16_t* wg, const float* bias, int T, int d,
+                        moe_route_params p, int32_t* idx, float* w, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  clear_error();
+  REQUIRE(T >= 0, "T=%d is negative", T);
+  moe_status s = check_route_params(p);
+  if (s != MOE_OK) return s;
+  REQUIRE(d >= 128 && d % 128 == 0, "d=%d must be a positive multiple of 128", d);
+  if (T == 0) return MOE_OK;
+  REQUIRE(T <= INT32_MAX / p.topk, "T*k overflows int32");
+  REQUIRE((uint64_t)T * (uint64_t)d * 2u <= 0xFFFFFFFFull, "x of T=%d rows x d=%d exceeds 4 GiB", T, d);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(wg);
+  REQUIRE_ALIGNED4_OR_NULL(bias);
+  REQUIRE_PTR4(idx);
+  REQUIRE_PTR4(w);
+  const size_t need = moe::route_workspace_bytes(T, p.n_experts);
+  if (need > 0) {
+    if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0 || workspace_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "workspace %p of %zu bytes: %zu bytes, 4-byte aligned, needed", workspace,
+                  workspace_bytes, need);
+  }
+  return hip_status(moe::launch_route_ws(x, wg, bias, T, d, p.n_experts, p.n_groups, p.topk_groups,
+                                         p.topk, p.route_scale, idx, w,
+                                         need > 0 ? static_cast<float*>(workspace) : nullptr,
+                                         static_cast<hipStream_t>(stream)),
+                    "moe_route_ws launch");
 }
 
 namespace {

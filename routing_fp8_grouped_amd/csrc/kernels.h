@@ -17,6 +17,10 @@ hipError_t launch_quant_128x128(const uint16_t* w, int N, int K, uint8_t* q, flo
 hipError_t launch_route(const uint16_t* x, const uint16_t* wg, const float* bias, int T, int d,
                         int E, int G, int M, int k, float route_scale, int32_t* idx, float* w,
                         hipStream_t stream);
+size_t route_workspace_bytes(int T, int E);
+hipError_t launch_route_ws(const uint16_t* x, const uint16_t* wg, const float* bias, int T, int d, int E,
+                           int G, int M, int k, float route_scale, int32_t* idx, float* w, float* logits,
+                           hipStream_t stream);
 
 size_t permute_workspace_bytes(int T, int E);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const uint8_t* xq,

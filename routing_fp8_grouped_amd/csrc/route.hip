@@ -58,112 +58,13 @@ __device__ __forceinline__ float sigmoid32(float l) {
   return __builtin_amdgcn_rcpf(1.0f + expf(-l));
 }
 
-__global__ __launch_bounds__(RT_THREADS) void route_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ wg,
-                                                           const float* __restrict__ bias, int T,
-                                                           int d, int E, int G, int M, int k,
-                                                           double route_scale,
-                                                           int32_t* __restrict__ idx,
-                                                           float* __restrict__ wout) {
-  // ring of RT_NST stages; after the logits it holds the FP32 logit table
-  __shared__ __attribute__((aligned(16))) unsigned char ring[RT_NST * RT_STG];
-  __shared__ float gscore[RT_MAXG][RT_TOK];
-  __shared__ float sbias[RT_EXP];
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g16 = lane >> 4, r16 = lane & 15;
-  const int t0 = blockIdx.x * RT_TOK;
-  const int n_ks = d / RT_KS;
-  if (threadIdx.x < RT_EXP) sbias[threadIdx.x] = (bias && (int)threadIdx.x < E) ? bias[threadIdx.x] : 0.0f;
-
-  // ---- logits ----
-  // Direct loads: an instruction writes 1 KB = 16 rows of 64 bytes; lane l
-  // fills row 16 i + l / 4, physical chunk l % 4 with the logical chunk
-  // (l % 4) ^ ((row >> 2) & 3).  Wave w loads expert rows 32 w .. 32 w + 31 (its
-  // own experts) and, for w < 4, token rows 16 w .. 16 w + 15; rows past T or E
-  // repeat the last valid row (their results are never used).
-  const int pc = lane & 3;
-  uint32_t a_off = 0, b_off[2];
-  if (wave < 4) {
-    const int r = wave * 16 + (lane >> 2);
-    const int t = min(t0 + r, T - 1);
-    a_off = (uint32_t)t * (uint32_t)d * 2u + (uint32_t)((pc ^ ((r >> 2) & 3)) * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = wave * 32 + i * 16 + (lane >> 2);
-    const int e = min(r, E - 1);
-    b_off[i] = (uint32_t)e * (uint32_t)d * 2u + (uint32_t)((pc ^ ((r >> 2) & 3)) * 16);
-  }
-  const uint32_t ring0 = lds_addr(ring);
-#define RT_ISSUE(ks_)                                                                        \
-  do {                                                                                       \
-    const int ks__ = (ks_);                                                                  \
-    const uint32_t base__ = ring0 + (ks__ % RT_NST) * RT_STG;                                \
-    if (wave < 4) dma16(x + (size_t)ks__ * RT_KS, a_off, base__ + wave * 1024);              \
-    dma16(wg + (size_t)ks__ * RT_KS, b_off[0], base__ + RT_A + (wave * 2) * 1024);           \
-    dma16(wg + (size_t)ks__ * RT_KS, b_off[1], base__ + RT_A + (wave * 2 + 1) * 1024);       \
-  } while (0)
-
-  double acc64[4][2][4];
-  v4f acc[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc64[mt][nt][i] = 0.0;
-    }
-
-  // stages 0 .. RT_NST-2 in flight (d >= 128, so n_ks >= 4)
-  for (int ks = 0; ks < RT_NST - 1 && ks < n_ks; ++ks) RT_ISSUE(ks);
-  for (int ks = 0; ks < n_ks; ++ks) {
-    // stage ks has landed once at most the younger stages are outstanding
-    const int younger = min(RT_NST - 2, n_ks - 1 - ks);
-    if (younger >= RT_NST - 2) {
-      if (wave < 4) rt_wait_vmcnt<3 * (RT_NST - 2)>(); else rt_wait_vmcnt<2 * (RT_NST - 2)>();
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the tail of the loop
-    }
-    asm volatile("s_barrier" ::: "memory");   // all waves' loads visible; stage ks-1 free
-    if (ks + RT_NST - 1 < n_ks) RT_ISSUE(ks + RT_NST - 1);
-    const unsigned char* A = ring + (ks % RT_NST) * RT_STG;
-    const unsigned char* B = A + RT_A;
-    v8bf af[4], bf[2];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) af[mt] = rt_frag(A, mt * 16 + r16, g16);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) bf[nt] = rt_frag(B, wave * 32 + nt * 16 + r16, g16);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_bf16_16x16x32(af[mt], bf[nt], acc[mt][nt]);
-    if ((ks & 3) == 3) {   // a 128-wide chunk of d is complete: promote to FP64
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc64[mt][nt][i] += (double)acc[mt][nt][i];
-          acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-  }
-#undef RT_ISSUE
-  __syncthreads();   // every wave is done with the ring
-
-  // FP32 logit table [token][expert] over the ring
-  float* logit = reinterpret_cast<float*>(ring);
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        logit[(mt * 16 + g16 * 4 + i) * RT_LSTRIDE + wave * 32 + nt * 16 + r16] = (float)acc64[mt][nt][i];
-  __syncthreads();
-
+// Selection and gates of 64 tokens from their FP32 logit table in LDS
+// (token-major, row stride RT_LSTRIDE): called by all 512 threads.
+__device__ __forceinline__ void route_select_tile(const float* logit, const float* sbias,
+                                                  float (*gscore)[RT_TOK], int t0, int T, int E, int G,
+                                                  int M, int k, double route_scale,
+                                                  int32_t* __restrict__ idx, float* __restrict__ wout,
+                                                  int wave, int lane) {
   // ---- selection: a team of 8 lanes per token (wave w, lanes 8 j .. 8 j + 7
   // route token 8 w + j); member m handles the groups g = m mod 8 ----
   // Biased scores z = sigmoid(l) + b in FP32 (within ~1e-7 of the exact
@@ -307,12 +208,287 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(const uint16_t* __res
   }
 }
 
+__global__ __launch_bounds__(RT_THREADS) void route_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wg,
+                                                           const float* __restrict__ bias, int T,
+                                                           int d, int E, int G, int M, int k,
+                                                           double route_scale,
+                                                           int32_t* __restrict__ idx,
+                                                           float* __restrict__ wout) {
+  // ring of RT_NST stages; after the logits it holds the FP32 logit table
+  __shared__ __attribute__((aligned(16))) unsigned char ring[RT_NST * RT_STG];
+  __shared__ float gscore[RT_MAXG][RT_TOK];
+  __shared__ float sbias[RT_EXP];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int t0 = blockIdx.x * RT_TOK;
+  const int n_ks = d / RT_KS;
+  if (threadIdx.x < RT_EXP) sbias[threadIdx.x] = (bias && (int)threadIdx.x < E) ? bias[threadIdx.x] : 0.0f;
+
+  // ---- logits ----
+  // Direct loads: an instruction writes 1 KB = 16 rows of 64 bytes; lane l
+  // fills row 16 i + l / 4, physical chunk l % 4 with the logical chunk
+  // (l % 4) ^ ((row >> 2) & 3).  Wave w loads expert rows 32 w .. 32 w + 31 (its
+  // own experts) and, for w < 4, token rows 16 w .. 16 w + 15; rows past T or E
+  // repeat the last valid row (their results are never used).
+  const int pc = lane & 3;
+  uint32_t a_off = 0, b_off[2];
+  if (wave < 4) {
+    const int r = wave * 16 + (lane >> 2);
+    const int t = min(t0 + r, T - 1);
+    a_off = (uint32_t)t * (uint32_t)d * 2u + (uint32_t)((pc ^ ((r >> 2) & 3)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wave * 32 + i * 16 + (lane >> 2);
+    const int e = min(r, E - 1);
+    b_off[i] = (uint32_t)e * (uint32_t)d * 2u + (uint32_t)((pc ^ ((r >> 2) & 3)) * 16);
+  }
+  const uint32_t ring0 = lds_addr(ring);
+#define RT_ISSUE(ks_)                                                                        \
+  do {                                                                                       \
+    const int ks__ = (ks_);                                                                  \
+    const uint32_t base__ = ring0 + (ks__ % RT_NST) * RT_STG;                                \
+    if (wave < 4) dma16(x + (size_t)ks__ * RT_KS, a_off, base__ + wave * 1024);              \
+    dma16(wg + (size_t)ks__ * RT_KS, b_off[0], base__ + RT_A + (wave * 2) * 1024);           \
+    dma16(wg + (size_t)ks__ * RT_KS, b_off[1], base__ + RT_A + (wave * 2 + 1) * 1024);       \
+  } while (0)
+
+  double acc64[4][2][4];
+  v4f acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc64[mt][nt][i] = 0.0;
+    }
+
+  // stages 0 .. RT_NST-2 in flight (d >= 128, so n_ks >= 4)
+  for (int ks = 0; ks < RT_NST - 1 && ks < n_ks; ++ks) RT_ISSUE(ks);
+  for (int ks = 0; ks < n_ks; ++ks) {
+    // stage ks has landed once at most the younger stages are outstanding
+    const int younger = min(RT_NST - 2, n_ks - 1 - ks);
+    if (younger >= RT_NST - 2) {
+      if (wave < 4) rt_wait_vmcnt<3 * (RT_NST - 2)>(); else rt_wait_vmcnt<2 * (RT_NST - 2)>();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the tail of the loop
+    }
+    asm volatile("s_barrier" ::: "memory");   // all waves' loads visible; stage ks-1 free
+    if (ks + RT_NST - 1 < n_ks) RT_ISSUE(ks + RT_NST - 1);
+    const unsigned char* A = ring + (ks % RT_NST) * RT_STG;
+    const unsigned char* B = A + RT_A;
+    v8bf af[4], bf[2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) af[mt] = rt_frag(A, mt * 16 + r16, g16);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) bf[nt] = rt_frag(B, wave * 32 + nt * 16 + r16, g16);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_bf16_16x16x32(af[mt], bf[nt], acc[mt][nt]);
+    if ((ks & 3) == 3) {   // a 128-wide chunk of d is complete: promote to FP64
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc64[mt][nt][i] += (double)acc[mt][nt][i];
+          acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+  }
+#undef RT_ISSUE
+  __syncthreads();   // every wave is done with the ring
+
+  // FP32 logit table [token][expert] over the ring
+  float* logit = reinterpret_cast<float*>(ring);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        logit[(mt * 16 + g16 * 4 + i) * RT_LSTRIDE + wave * 32 + nt * 16 + r16] = (float)acc64[mt][nt][i];
+  __syncthreads();
+
+  route_select_tile(logit, sbias, gscore, t0, T, E, G, M, k, route_scale, idx, wout, wave, lane);
+}
+
 hipError_t launch_route(const uint16_t* x, const uint16_t* wg, const float* bias, int T, int d,
                         int E, int G, int M, int k, float route_scale, int32_t* idx, float* w,
                         hipStream_t stream) {
   const int blocks = (T + RT_TOK - 1) / RT_TOK;
   hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(RT_THREADS), 0, stream, x, wg, bias, T, d, E, G, M,
                      k, (double)route_scale, idx, w);
+  return hipGetLastError();
+}
+
+// ---- two-kernel form for small batches (a workspace holds the logits) ----
+// route_logits_kernel: workgroup (token block of TM, expert block of EN) computes
+// those logits over all of d, so a batch of few tokens spreads the centroid
+// stream over E / EN workgroups instead of one.  The arithmetic per logit is
+// that of route_kernel: 16x16x32 BF16 MFMAs in d order, the FP32 partial of
+// each 128-wide chunk added to an FP64 sum in chunk order, the sum rounded
+// once to FP32; so both forms give the same logits.  Stages of 128 elements
+// of d (256-byte rows, 16-byte chunk c of row r at c ^ (r & 15)).
+constexpr int RL_KS = 128;                    // d elements per stage
+constexpr int RL_ROWB = RL_KS * 2;            // 256-byte rows
+constexpr int RL_NST = 4;                     // ring depth
+
+__device__ __forceinline__ int rl_off(int r, int c) { return r * RL_ROWB + ((c ^ (r & 15)) << 4); }
+
+template <int TM, int EN, int NW>
+__global__ __launch_bounds__(NW * 64) void route_logits_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wg, int T,
+                                                                 int d, int E, float* __restrict__ logits) {
+  constexpr int ROWS = TM + EN;
+  constexpr int STG = ROWS * RL_ROWB;
+  constexpr int NINSTR = ROWS / 4;            // 1 KB direct loads per stage: 4 rows each
+  constexpr int NTE = EN / 16;                // expert tiles
+  constexpr int TPW = (TM / 16) * NTE / NW;   // 16x16 tiles per wave
+  static_assert(TPW >= 1 && (TM / 16) * NTE == TPW * NW, "tile split");
+  __shared__ __attribute__((aligned(16))) unsigned char ring[RL_NST * STG];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int t0 = blockIdx.x * TM, e0 = blockIdx.y * EN;
+  const int n_ks = d / RL_KS;
+  // this lane's source rows: instruction i (of this wave) fills rows 4 j .. 4 j + 3
+  // with j = wave + NW * i; lane l writes row 4 j + l / 16, physical chunk l % 16
+  constexpr int IPW = (NINSTR + NW - 1) / NW;
+  uint32_t src[IPW];
+  const uint16_t* base[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int j = wave + NW * i;
+    const int r = 4 * j + (lane >> 4);
+    const int lc = (lane & 15) ^ (r & 15);
+    if (r < TM) {
+      base[i] = x;
+      src[i] = (uint32_t)min(t0 + r, T - 1) * (uint32_t)d * 2u + lc * 16;
+    } else {
+      base[i] = wg;
+      src[i] = (uint32_t)min(e0 + r - TM, E - 1) * (uint32_t)d * 2u + lc * 16;
+    }
+  }
+  const uint32_t ring0 = lds_addr(ring);
+  auto issue = [&](int ks) {
+    const uint32_t st = ring0 + (ks % RL_NST) * STG;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int j = wave + NW * i;
+      if (j < NINSTR) dma16(base[i] + (size_t)ks * RL_KS, src[i], st + j * 1024);
+    }
+  };
+  v4f acc[TPW];
+  double acc64[TPW][4];
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc64[q][i] = 0.0;
+  }
+  for (int ks = 0; ks < RL_NST - 1 && ks < n_ks; ++ks) issue(ks);
+  for (int ks = 0; ks < n_ks; ++ks) {
+    // stage ks has landed once this wave's loads of it are done (the younger
+    // stages may stay in flight); the barrier makes every wave's visible
+    const int younger = min(RL_NST - 2, n_ks - 1 - ks);
+    if (younger == RL_NST - 2) {
+      constexpr int OUT = (RL_NST - 2) * IPW;   // upper bound of this wave's younger loads
+      rt_wait_vmcnt<OUT>();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    }
+    asm volatile("s_barrier" ::: "memory");
+    if (ks + RL_NST - 1 < n_ks) issue(ks + RL_NST - 1);
+    const unsigned char* S = ring + (ks % RL_NST) * STG;
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const int id = wave * TPW + q;
+      const int mt = id / NTE, nt = id - (id / NTE) * NTE;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const v8bf af = *reinterpret_cast<const v8bf*>(S + rl_off(mt * 16 + r16, kk * 4 + g16));
+        const v8bf bf = *reinterpret_cast<const v8bf*>(S + rl_off(TM + nt * 16 + r16, kk * 4 + g16));
+        acc[q] = mfma_bf16_16x16x32(af, bf, acc[q]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc64[q][i] += (double)acc[q][i];
+      acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int id = wave * TPW + q;
+    const int mt = id / NTE, nt = id - (id / NTE) * NTE;
+    const int e = e0 + nt * 16 + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + mt * 16 + g16 * 4 + i;
+      if (t < T && e < E) logits[(size_t)t * E + e] = (float)acc64[q][i];
+    }
+  }
+}
+
+// Selection of 64 tokens from the logits of route_logits_kernel.
+__global__ __launch_bounds__(RT_THREADS) void route_select_kernel(const float* __restrict__ logits,
+                                                                  const float* __restrict__ bias, int T,
+                                                                  int E, int G, int M, int k,
+                                                                  double route_scale,
+                                                                  int32_t* __restrict__ idx,
+                                                                  float* __restrict__ wout) {
+  __shared__ float logit[RT_TOK * RT_LSTRIDE];
+  __shared__ float gscore[RT_MAXG][RT_TOK];
+  __shared__ float sbias[RT_EXP];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * RT_TOK;
+  if (threadIdx.x < RT_EXP) sbias[threadIdx.x] = (bias && (int)threadIdx.x < E) ? bias[threadIdx.x] : 0.0f;
+  // all of a thread's loads in flight at once (the table was just written by
+  // workgroups on other XCDs: every load is a far miss)
+  constexpr int PER = RT_TOK * RT_EXP / RT_THREADS;
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * RT_THREADS;
+    const int r = i / E, e = i - r * E;
+    v[j] = i < RT_TOK * E ? logits[(size_t)min(t0 + r, T - 1) * E + e] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * RT_THREADS;
+    const int r = i / E, e = i - r * E;
+    if (i < RT_TOK * E) logit[r * RT_LSTRIDE + e] = v[j];
+  }
+  __syncthreads();
+  route_select_tile(logit, sbias, gscore, t0, T, E, G, M, k, route_scale, idx, wout, wave, lane);
+}
+
+// Token counts up to which the two-kernel form is used, and its tile shapes.
+constexpr int RS_SMALL_T = 1024;   // 16 tokens x 32 experts per workgroup
+constexpr int RS_MAX_T = 8192;     // 64 tokens x 64 experts per workgroup
+
+size_t route_workspace_bytes(int T, int E) {
+  if (T <= 0 || T > RS_MAX_T) return 0;
+  return ((size_t)T * (size_t)E * 4 + 255) & ~(size_t)255;
+}
+
+hipError_t launch_route_ws(const uint16_t* x, const uint16_t* wg, const float* bias, int T, int d, int E,
+                           int G, int M, int k, float route_scale, int32_t* idx, float* w, float* logits,
+                           hipStream_t stream) {
+  if (T > RS_MAX_T || logits == nullptr)
+    return launch_route(x, wg, bias, T, d, E, G, M, k, route_scale, idx, w, stream);
+  if (T <= RS_SMALL_T)
+    hipLaunchKernelGGL((route_logits_kernel<16, 32, 2>), dim3((T + 15) / 16, (E + 31) / 32), dim3(128), 0,
+                       stream, x, wg, T, d, E, logits);
+  else
+    hipLaunchKernelGGL((route_logits_kernel<64, 64, 8>), dim3((T + 63) / 64, (E + 63) / 64), dim3(512), 0,
+                       stream, x, wg, T, d, E, logits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_select_kernel, dim3((T + RT_TOK - 1) / RT_TOK), dim3(RT_THREADS), 0, stream, logits,
+                     bias, T, E, G, M, k, (double)route_scale, idx, w);
   return hipGetLastError();
 }
 

@@ -38,6 +38,8 @@ KERNELS = {
     "grouped_gemm_small_kernel<true, true>": "grouped_gemm_fp8_up_e8m0 (few rows)",
     "grouped_gemm_small_kernel<false, false>": "grouped_gemm_fp8_down (few rows)",
     "route_kernel": "moe_route",
+    "route_logits_kernel": "moe_route_ws (logits)",
+    "route_select_kernel": "moe_route_ws (select)",
     "quant_1x128_kernel<false>": "fp8_quant_1x128",
     "quant_128x128_kernel<false>": "fp8_quant_128x128",
     "quant_1x128_kernel<true>": "fp8_quant_1x128_pow2",

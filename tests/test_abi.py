@@ -25,7 +25,8 @@ def last(lib):
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.header_symbols()
-    assert set(declared) == {"moe_route", "fp8_quant_1x128", "fp8_quant_128x128",
+    assert set(declared) == {"moe_route", "moe_route_workspace_bytes", "moe_route_ws",
+                             "fp8_quant_1x128", "fp8_quant_128x128",
                              "moe_permute_workspace_bytes", "moe_permute",
                              "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up",
                              "grouped_gemm_fp8_down", "moe_combine", "moe_bias_update",
@@ -79,6 +80,26 @@ def test_route_null_and_alignment(lib):
     assert lib.moe_route(A, A, None, -1, 256, rp(), A, A, None) == 1
     # T = 0: successful no-op even with null pointers
     assert lib.moe_route(None, None, None, 0, 256, rp(), None, None, None) == 0
+
+
+def test_route_ws_workspace(lib):
+    assert lib.moe_route_workspace_bytes(64, 256) == 64 * 256 * 4
+    assert lib.moe_route_workspace_bytes(100, 16) == 6400 + 0   # 100*16*4 rounded up to 256
+    assert lib.moe_route_workspace_bytes(8192, 256) == 8192 * 256 * 4
+    assert lib.moe_route_workspace_bytes(8193, 256) == 0          # single-kernel form
+    assert lib.moe_route_workspace_bytes(0, 256) == 0
+    assert lib.moe_route_workspace_bytes(64, 300) == 0
+    # a workspace is required where the two-kernel form runs
+    st = lib.moe_route_ws(A, A, None, 10, 256, rp(), A, A, None, 0, None)
+    assert st == 3 and "workspace" in last(lib)
+    st = lib.moe_route_ws(A, A, None, 10, 256, rp(), A, A, A, 100, None)
+    assert st == 3 and "workspace" in last(lib)
+    st = lib.moe_route_ws(A, A, None, 10, 256, rp(), A, A, MIS4, 1 << 20, None)
+    assert st == 3 and "aligned" in last(lib)
+    # the same argument checks as moe_route
+    assert lib.moe_route_ws(None, A, None, 10, 256, rp(), A, A, A, 1 << 20, None) == 1
+    assert lib.moe_route_ws(A, A, None, 10, 100, rp(), A, A, A, 1 << 20, None) == 1 and "d=100" in last(lib)
+    assert lib.moe_route_ws(None, None, None, 0, 256, rp(), None, None, None, 0, None) == 0
 
 
 def test_quant_validation(lib):

@@ -141,6 +141,29 @@ def test_route_parity(T, d, E, G, M, k, rho):
     assert np.allclose(gw.astype(np.float64).sum(1), rho, rtol=1e-5)
 
 
+@pytest.mark.parametrize("T,d,E,G,M,k", [
+    (1, 7168, 256, 8, 4, 8), (64, 7168, 256, 8, 4, 8), (100, 7168, 256, 8, 4, 8),
+    (1024, 7168, 256, 8, 4, 8), (1025, 7168, 256, 8, 4, 8), (4096, 7168, 256, 8, 4, 8),
+    (8192, 512, 256, 8, 4, 8), (8193, 256, 64, 8, 4, 8), (300, 384, 12, 3, 1, 2),
+    (70, 256, 256, 16, 4, 16), (65, 128, 40, 8, 2, 4)])
+def test_route_ws_matches_single_kernel(T, d, E, G, M, k):
+    """The two-kernel router (workspace) returns moe_route's result bit for bit:
+    the same logit arithmetic, the same selection code."""
+    log(f"route_ws T={T} d={d} E={E} G={G} M={M} k={k}")
+    rng = np.random.default_rng(T + 7 * E + d)
+    x = bf16_tensor(rng.standard_normal((T, d))).to(DEV)
+    wg = bf16_tensor(rng.standard_normal((E, d)) / np.sqrt(d)).to(DEV)
+    b = torch.from_numpy(rng.uniform(-0.05, 0.05, E).astype(np.float32)).to(DEV)
+    out = []
+    for ws in (None, torch.empty(max(16, moe.moe_route_workspace_bytes(T, E)), dtype=torch.uint8, device=DEV)):
+        idx = torch.full((T, k), -1, dtype=torch.int32, device=DEV)
+        w = torch.full((T, k), -1.0, dtype=torch.float32, device=DEV)
+        moe.moe_route(x, wg, b, G, M, k, 2.5, idx, w, workspace=ws)
+        out.append((idx, w))
+    torch.cuda.synchronize()
+    assert torch.equal(out[0][0], out[1][0]) and torch.equal(out[0][1], out[1][1])
+
+
 def test_route_bias_only_moves_selection():
     """A bias that pushes every unselected expert down keeps the selection and
     leaves the gates bit-identical (the bias never enters the weights)."""
