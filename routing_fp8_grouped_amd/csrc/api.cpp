@@ -72,9 +72,6 @@ moe_status check_route_params(const moe_route_params& p) {
           p.topk, p.topk_groups * per);
   REQUIRE(std::isfinite(p.route_scale), "route_scale is not finite");
   if (p.topk > 16) return fail(MOE_ERR_UNSUPPORTED, "topk=%d > 16 is not implemented", p.topk);
-  if (p.topk / p.topk_groups > 8)
-    return fail(MOE_ERR_UNSUPPORTED, "topk/topk_groups=%d > 8 is not implemented",
-                p.topk / p.topk_groups);
   return MOE_OK;
 }
 

@@ -58,6 +58,111 @@ __device__ __forceinline__ float sigmoid32(float l) {
   return __builtin_amdgcn_rcpf(1.0f + expf(-l));
 }
 
+// Selection for 8 groups of 32 experts and k <= 8 (the V3 shape), with the
+// results of the general code below: member m of a token's team owns group m
+// and keeps its 32 biased scores in registers; the group score sums the n_top
+// largest in descending order; the top-k are taken in k rounds of a per-member
+// argmax (ties to the lower id) and a team argmax (larger score, then lower
+// id), i.e. in the order of the general merge; member m then computes the gate
+// of the m-th selected expert in FP64, the team sums them by the same
+// shuffles.
+__device__ __forceinline__ void route_select_g8(const float* L, const float* sbias, float (*gscore)[RT_TOK],
+                                                int tt, int t, int T, int M, int k, int n_top,
+                                                double route_scale, int32_t* __restrict__ idx,
+                                                float* __restrict__ wout, int mem) {
+  const float NEG = -__builtin_huge_valf();
+  constexpr int NONE = 0x7fffffff;
+  float z[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) z[i] = sigmoid32(L[mem * 32 + i]) + sbias[mem * 32 + i];
+  {
+    float top[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) top[i] = NEG;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      float v = z[e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < n_top && v > top[i]) {
+          const float tmp = top[i];
+          top[i] = v;
+          v = tmp;
+        }
+      }
+    }
+    float gs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < n_top) gs += top[i];
+    gscore[mem][tt] = gs;
+  }
+  wave_sync_lds();
+  uint32_t gmask = 0;
+  for (int r = 0; r < M; ++r) {
+    float bv = NEG;
+    int bg = -1;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const float v = gscore[g][tt];
+      if (!((gmask >> g) & 1u) && (bg < 0 || v > bv)) {
+        bv = v;
+        bg = g;
+      }
+    }
+    gmask |= 1u << bg;
+  }
+  const bool kept = (gmask >> mem) & 1u;
+  uint32_t taken = 0;
+  int sel[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    sel[r] = NONE;
+    if (r < k) {
+      float bv = NEG;
+      int bi = NONE;
+      if (kept) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (!((taken >> i) & 1u) && (bi == NONE || z[i] > bv)) {
+            bv = z[i];
+            bi = mem * 32 + i;
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        const bool take = (oi != NONE) && (bi == NONE || ov > bv || (ov == bv && oi < bi));
+        if (take) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      sel[r] = bi;
+      if ((bi >> 5) == mem) taken |= 1u << (bi & 31);
+    }
+  }
+  int mine = sel[0];
+#pragma unroll
+  for (int r = 1; r < 8; ++r)
+    if (mem == r) mine = sel[r];
+  double s_mine = 0.0;
+  if (mem < k) s_mine = 1.0 / (1.0 + exp(-(double)L[mine]));
+  double ssum = 0.0 + s_mine;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) ssum += __shfl_xor(ssum, o);
+  if (t < T && mem < k) {
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k && sel[j] < mine) ++rank;
+    idx[(size_t)t * k + rank] = mine;
+    wout[(size_t)t * k + rank] = (float)(route_scale * s_mine / ssum);
+  }
+}
+
 // Selection and gates of 64 tokens from their FP32 logit table in LDS
 // (token-major, row stride RT_LSTRIDE): called by all 512 threads.
 __device__ __forceinline__ void route_select_tile(const float* logit, const float* sbias,
@@ -77,15 +182,19 @@ __device__ __forceinline__ void route_select_tile(const float* logit, const floa
   const int per = E / G;
   const int n_top = k / M;
   const float NEG = -__builtin_huge_valf();
-  // 1. group scores: sum of the n_top largest biased scores of each group
+  if (G == 8 && per == 32 && k <= 8) {   // uniform: the V3 shape
+    route_select_g8(L, sbias, gscore, tt, t, T, M, k, n_top, route_scale, idx, wout, mem);
+    return;
+  }
+  // 1. group scores: sum of the n_top (<= k <= 16) largest biased scores of each group
   for (int g = mem; g < G; g += 8) {
-    float top[8];
+    float top[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) top[i] = NEG;
+    for (int i = 0; i < 16; ++i) top[i] = NEG;
     for (int e = g * per; e < (g + 1) * per; ++e) {
       float v = sigmoid32(L[e]) + sbias[e];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 16; ++i) {
         if (i < n_top && v > top[i]) {
           const float tmp = top[i];
           top[i] = v;
@@ -95,7 +204,7 @@ __device__ __forceinline__ void route_select_tile(const float* logit, const floa
     }
     float gs = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 16; ++i)
       if (i < n_top) gs += top[i];
     gscore[g][tt] = gs;
   }

@@ -113,6 +113,8 @@ ROUTE_CASES = [
     (70, 256, 256, 16, 4, 16, 2.5),
     (65, 256, 32, 32, 8, 8, 1.0),
     (1, 128, 4, 1, 1, 4, 2.5),
+    (50, 256, 64, 2, 1, 16, 2.5),      # group score over k/M = 16 experts
+    (90, 256, 256, 8, 2, 6, 1.0),      # 8 groups of 32, k < 8
 ]
 
 
