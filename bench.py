@@ -215,6 +215,11 @@ def main():
     up_bytes = (touched * (2 * cfg.f * cfg.d + (2 * cfg.f // 128) * (cfg.d // 128) * 4)
                 + cfg.T * (cfg.d + cfg.d // 128 * 4) + rows * (cfg.f + cfg.f // 128 * 4))
     up_s = stage_ms["gemm_up"] * 1e-3
+    # the library streams the weights (grouped_gemm_small_kernel) when the
+    # experts average at most 16 rows, and tiles otherwise
+    small = rows <= 16 * (cfg.E + 1)
+    up_kernel = ("grouped_gemm_fp8_up (grouped_gemm_small_kernel<true, false>)" if small
+                 else "grouped_gemm_fp8_up (grouped_gemm_kernel<true, false>)")
     if up_flop / up_bytes >= FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
         roof = {"bound": "mfma", "achieved": up_flop / up_s / 1e12, "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
@@ -241,7 +246,7 @@ def main():
                    "groups_per_token": cfg.M, "topk": cfg.k, "d_ffn": cfg.f,
                    "route_scale": cfg.route_scale, "dispatch_copy": args.dispatch},
         "roofline": dict(roof, traffic=traffic,
-                         kernel="grouped_gemm_fp8_up (grouped_gemm_kernel<true, false>)",
+                         kernel=up_kernel,
                          flop_per_launch=up_flop, algorithmic_bytes_per_launch=up_bytes,
                          avg_launch_ms=stage_ms["gemm_up"], tflops=up_tflops),
         "stages_ms": stage_ms,
@@ -297,7 +302,8 @@ def main():
             "value": cfg.T / (ms8 * 1e-3), "unit": "tokens/s", "ms_per_step": ms8,
             "stages_ms": st8, "gemm_up_tflops": up8, "gemm_up_frac_of_fp8_peak": up8 / FP8_PEAK_TFLOPS,
             "grouped_gemm_tflops": (up_flop + down_flop) / ((st8["gemm_up"] + st8["gemm_down"]) * 1e-3) / 1e12,
-            "kernel": "grouped_gemm_fp8_up_e8m0 (grouped_gemm_kernel<true, true>)",
+            "kernel": ("grouped_gemm_fp8_up_e8m0 (grouped_gemm_small_kernel<true, true>)" if small
+                       else "grouped_gemm_fp8_up_e8m0 (grouped_gemm_kernel<true, true>)"),
         }
         del W8, layer8
     if not args.no_cpu_baseline:
