@@ -48,9 +48,10 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def read_traffic(workload):
+def read_traffic(workload, kernel):
     """HBM bytes per launch of the first expert GEMM from the committed PMC
-    summary, if it was taken on the current kernel source (else None)."""
+    summary, if it was taken on this kernel and its current source (else
+    None)."""
     path = os.path.join(ROOT, "profiles", f"grouped_gemm_up_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -60,7 +61,9 @@ def read_traffic(workload):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != profiling.gemm_source_hash():
+    if vals.get("kernel", profiling.TILED) != kernel:
+        return None
+    if vals.get("kernel_source_sha256_16") != profiling.gemm_source_hash(kernel):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -209,7 +212,6 @@ def main():
     gemm_tflops = (up_flop + down_flop) / ((stage_ms["gemm_up"] + stage_ms["gemm_down"]) * 1e-3) / 1e12
     touched = int((counts > 0).sum()) + 1
     weight_bytes = touched * (3 * cfg.d * cfg.f + 3 * (cfg.d // 128) * (cfg.f // 128) * 4)
-    traffic = read_traffic(cfg.name)
     # algorithmic bytes of the first expert GEMM: each touched expert's W1/W3
     # codes and scales once, the token rows once, h and its scales written once
     up_bytes = (touched * (2 * cfg.f * cfg.d + (2 * cfg.f // 128) * (cfg.d // 128) * 4)
@@ -220,6 +222,7 @@ def main():
     small = rows <= 16 * (cfg.E + 1)
     up_kernel = ("grouped_gemm_fp8_up (grouped_gemm_small_kernel<true, false>)" if small
                  else "grouped_gemm_fp8_up (grouped_gemm_kernel<true, false>)")
+    traffic = read_traffic(cfg.name, profiling.STREAMING if small else profiling.TILED)
     if up_flop / up_bytes >= FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
         roof = {"bound": "mfma", "achieved": up_flop / up_s / 1e12, "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}

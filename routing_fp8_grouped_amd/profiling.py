@@ -9,7 +9,8 @@
 counts and durations.
 
 ``traffic`` turns two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
-runs of ``bench.py`` into HBM bytes per launch of the first expert GEMM.  Both
+runs of ``bench.py`` into HBM bytes per launch of the first expert GEMM (the
+tiled kernel, or with ``--kernel`` the weight-streaming one of small batches).  Both
 counters are in KiB per dispatch but count L2-to-memory requests, so each is
 scaled by what it reads for the 1 GiB elementwise copy ``bench.py`` runs
 before its timed region (1 GiB read and 1 GiB written): factor = 1 GiB /
@@ -28,7 +29,14 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-GEMM_SOURCES = ["routing_fp8_grouped_amd/csrc/gemm.hip", "routing_fp8_grouped_amd/csrc/common.h"]
+TILED = "grouped_gemm_kernel<true, false>"
+STREAMING = "grouped_gemm_small_kernel<true, false>"
+# sources whose hash identifies the kernel a traffic summary was taken on
+KERNEL_SOURCES = {
+    TILED: ["routing_fp8_grouped_amd/csrc/gemm.hip", "routing_fp8_grouped_amd/csrc/common.h"],
+    STREAMING: ["routing_fp8_grouped_amd/csrc/gemm_small.hip", "routing_fp8_grouped_amd/csrc/common.h"],
+}
+GEMM_SOURCES = KERNEL_SOURCES[TILED]
 KERNELS = {
     "grouped_gemm_kernel<true, false>": "grouped_gemm_fp8_up",
     "grouped_gemm_kernel<false, false>": "grouped_gemm_fp8_down",
@@ -54,10 +62,11 @@ KERNELS = {
 GIB_KIB = float(1 << 20)
 
 
-def gemm_source_hash():
-    """First 16 hex digits of the SHA-256 of the grouped GEMM's sources."""
+def gemm_source_hash(kernel=TILED):
+    """First 16 hex digits of the SHA-256 of the first expert GEMM's sources
+    (the tiled kernel, or the weight-streaming kernel of small batches)."""
     h = hashlib.sha256()
-    for p in GEMM_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -109,7 +118,7 @@ def per_dispatch(d, counter):
     return {k: (names[k], v) for k, v in vals.items()}
 
 
-def traffic(fetch_dir, write_dir, kernel_frag="grouped_gemm_kernel<true, false>"):
+def traffic(fetch_dir, write_dir, kernel_frag=TILED):
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         disp = per_dispatch(d, counter)
@@ -134,19 +143,21 @@ def main(argv=None):
     t.add_argument("--workload", required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
+    t.add_argument("--kernel", default=TILED, choices=sorted(KERNEL_SOURCES))
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(f"rocprofv3 kernel statistics\ncommand: {a.command}\n")
         print("\n".join(stats_table(a.dir)))
         return
-    r = traffic(a.fetch_dir, a.write_dir)
+    r = traffic(a.fetch_dir, a.write_dir, a.kernel)
     f, w = r["FETCH_SIZE"], r["WRITE_SIZE"]
     kf, kw = GIB_KIB / f["copy_kib"], GIB_KIB / w["copy_kib"]
     hbm = (f["kib_per_launch"] * kf + w["kib_per_launch"] * kw) * 1024
     print(f"grouped_gemm_fp8_up HBM traffic, workload {a.workload}")
     print(f"command_fetch: {a.command_fetch}")
     print(f"command_write: {a.command_write}")
-    print(f"kernel_source_sha256_16: {gemm_source_hash()}")
+    print(f"kernel: {a.kernel}")
+    print(f"kernel_source_sha256_16: {gemm_source_hash(a.kernel)}")
     print(f"launches: {f['launches']}")
     print(f"fetch_kib_per_launch: {f['kib_per_launch']:.1f}")
     print(f"write_kib_per_launch: {w['kib_per_launch']:.1f}")
