@@ -140,15 +140,21 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
 // Workgroup (cb, blk): columns [128 cb, 128 cb + 128) of padded block blk.
 // FP8IN: the source is a 1x128 FP8 tensor (codes + scales) whose row r of the
 // grouped order is row row_src[r] (or r when row_src is null); otherwise a BF16
-// tensor in grouped order.  Values are dequantised in FP32, each column's
-// 128-row amax gives a power-of-two scale, codes are E4M3(x / scale).
+// tensor in grouped order.  The tile is kept in LDS in its input form (FP8
+// codes with their row scales, or BF16), 19 or 35 KB, so several workgroups
+// share a CU; each column thread rebuilds its 64 FP32 values exactly (code x
+// scale in FP32, or the BF16 value), takes the column's 128-row amax, a
+// power-of-two scale, and codes E4M3(x / scale), staged in LDS (over the tile)
+// for whole 128-byte output rows.
 template <bool FP8IN>
 __global__ __launch_bounds__(256) void regroup_128x1_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint16_t* __restrict__ xb,
     const int32_t* __restrict__ row_src, const int32_t* __restrict__ offsets, int n_groups, int C,
     int Kp, uint8_t* __restrict__ out, float* __restrict__ out_s) {
+  constexpr int ROWB = FP8IN ? 144 : 272;   // padded row bytes of the input tile
   __shared__ int pb[BW_MAX_GROUPS + 1];
-  __shared__ __attribute__((aligned(16))) float tile[128][129];   // values, then [column][row] codes
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * ROWB];   // input tile, then [column][row] codes
+  __shared__ float rscale[FP8IN ? 128 : 1];
   __shared__ float colmax[2][128];
   const int tid = threadIdx.x, cb = blockIdx.x, blk = blockIdx.y;
   if (tid < 64) padded_block_prefix(offsets, n_groups, pb, tid);
@@ -159,38 +165,35 @@ __global__ __launch_bounds__(256) void regroup_128x1_kernel(
   const int nrows = min(128, offsets[e + 1] - row0);
   {
     const int r = tid >> 1, half = tid & 1;
-    float v[64];
-    if (r < nrows) {
-      if (FP8IN) {
+    if (FP8IN) {
+      uint4 q[4];
+      float sc = 0.0f;
+      if (r < nrows) {
         const int src = row_src ? row_src[row0 + r] : row0 + r;
-        const float s = xs[(size_t)src * (C / 128) + cb];
+        sc = xs[(size_t)src * (C / 128) + cb];
         const uint8_t* p = xq + (size_t)src * C + cb * 128 + half * 64;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 q = *reinterpret_cast<const uint4*>(p + i * 16);
-          const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-          for (int j = 0; j < 16; ++j) v[i * 16 + j] = e4m3_to_f32((u[j >> 2] >> (8 * (j & 3))) & 0xFFu) * s;
-        }
+        for (int i = 0; i < 4; ++i) q[i] = *reinterpret_cast<const uint4*>(p + i * 16);
       } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = make_uint4(0u, 0u, 0u, 0u);   // zero rows pad the block
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&tile[r * ROWB + half * 64 + i * 16]) = q[i];
+      if (half == 0) rscale[r] = sc;
+    } else {
+      uint4 q[8];
+      if (r < nrows) {
         const uint16_t* p = xb + (size_t)(row0 + r) * C + cb * 128 + half * 64;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint4 q = *reinterpret_cast<const uint4*>(p + i * 8);
-          const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+        for (int i = 0; i < 8; ++i) q[i] = *reinterpret_cast<const uint4*>(p + i * 8);
+      } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v[i * 8 + 2 * j] = bf16_to_f32((uint16_t)(u[j] & 0xFFFFu));
-            v[i * 8 + 2 * j + 1] = bf16_to_f32((uint16_t)(u[j] >> 16));
-          }
-        }
+        for (int i = 0; i < 8; ++i) q[i] = make_uint4(0u, 0u, 0u, 0u);
       }
-    } else {
 #pragma unroll
-      for (int i = 0; i < 64; ++i) v[i] = 0.0f;
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&tile[r * ROWB + half * 128 + i * 16]) = q[i];
     }
-#pragma unroll
-    for (int i = 0; i < 64; ++i) tile[r][half * 64 + i] = v[i];
   }
   __syncthreads();
   // column phase: thread (c, part) holds rows [64 part, 64 part + 64) of column c
@@ -199,11 +202,15 @@ __global__ __launch_bounds__(256) void regroup_128x1_kernel(
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
-    w[i] = tile[part * 64 + i][c];
+    const int rr = part * 64 + i;
+    if (FP8IN)
+      w[i] = e4m3_to_f32(tile[rr * ROWB + c]) * rscale[rr];
+    else
+      w[i] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(&tile[rr * ROWB + 2 * c]));
     amax = fmaxf(amax, fabsf(w[i]));
   }
   colmax[part][c] = amax;
-  __syncthreads();
+  __syncthreads();   // every read of the tile is done: its memory now holds the codes
   const float s = scale_from_amax_pow2(fmaxf(colmax[0][c], colmax[1][c]));
   const float inv = 1.0f / s;   // exact: s is a power of two
   uint32_t pk[16];
@@ -211,8 +218,7 @@ __global__ __launch_bounds__(256) void regroup_128x1_kernel(
   for (int j = 0; j < 16; ++j)
     pk[j] = f32x4_to_e4m3(w[4 * j] * inv, w[4 * j + 1] * inv, w[4 * j + 2] * inv, w[4 * j + 3] * inv);
   if (part == 0) out_s[(size_t)blk * C + cb * 128 + c] = s;
-  __syncthreads();   // every read of tile is done: its memory now holds the codes
-  uint8_t(*tq)[144] = reinterpret_cast<uint8_t(*)[144]>(&tile[0][0]);
+  uint8_t(*tq)[144] = reinterpret_cast<uint8_t(*)[144]>(&tile[0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<uint4*>(&tq[c][part * 64 + i * 16]) = make_uint4(pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]);
