@@ -138,6 +138,29 @@ def timed_steps(layer, x, wg, b, W, steps):
     return (t1 - t0) * 1e3 / steps, stage_ms
 
 
+def timed_graph(layer, x, wg, b, W, steps):
+    """Milliseconds per forward replayed from a HIP graph (the same launches
+    captured once; no launch gaps), bracketed by device synchronisations."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(x, wg, b, W)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, wg, b, W)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del g
+    return ms
+
+
 def timed_backward(layer, dout, Wt, steps):
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BWD_STAGES) + 1)] for _ in range(steps)]
@@ -203,6 +226,8 @@ def main():
     ms_per_step, stage_ms = timed_steps(layer, x, wg, b, W, args.steps)
     log(f"{args.steps} timed steps: {ms_per_step:.3f} ms/step; stages " +
         ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
+    graph_ms = timed_graph(layer, x, wg, b, W, args.steps)
+    log(f"graph replay: {graph_ms:.3f} ms/step")
 
     counts = np.bincount(layer.idx.cpu().numpy().reshape(-1), minlength=cfg.E)
     rows = cfg.rows
@@ -258,6 +283,8 @@ def main():
         "expert_rows": {"max": int(counts.max()), "min": int(counts.min()),
                         "experts_touched": touched},
         "weights_hbm_gbs": weight_bytes / (ms_per_step * 1e-3) / 1e9,
+        "graph_replay": {"ms_per_step": graph_ms, "tokens_per_s": cfg.T / (graph_ms * 1e-3),
+                         "note": "the same forward captured once in a HIP graph and replayed"},
         "context": "pages: 2.788M H800 GPU-hours for the whole V3 training run; "
                    "180K H800 GPU-hours per trillion training tokens (not comparable)",
     }
