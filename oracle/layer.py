@@ -67,11 +67,15 @@ def expert_ffn(xq, xs, w13q, w13s, w2q, w2s, rule="fp32"):
     return y, {"g": g, "u": u, "h": h, "hq": hq, "hs": hs}
 
 
-def combine(y_routed, w, y_shared):
-    """out[t] = BF16( sum_j w[t, j] * y_routed[t, j] + y_shared[t] ), float64 sum.
-    y_routed [T, k, d], w [T, k], y_shared [T, d]."""
+def combine(y_routed, w, y_shared, residual=None):
+    """out[t] = BF16( sum_j w[t, j] * y_routed[t, j] + y_shared[t] (+ residual[t]) ),
+    float64 sum, one rounding.  y_routed [T, k, d], w [T, k], y_shared [T, d],
+    residual [T, d] or None (the book's chapter 15 lists the residual path
+    among what combine adds; the layer itself passes none)."""
     acc = np.einsum("tk,tkd->td", np.asarray(w, np.float64), np.asarray(y_routed, np.float64))
     acc += np.asarray(y_shared, np.float64)
+    if residual is not None:
+        acc += np.asarray(residual, np.float64)
     return bf16_round(acc)
 
 

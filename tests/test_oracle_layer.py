@@ -43,6 +43,27 @@ def test_permute_brute_force(T, E, k):
             assert offsets[idx[t, j]] <= pos[t, j] < offsets[idx[t, j] + 1]
 
 
+
+def test_combine_residual():
+    """The residual path is added once, unscaled, inside the single rounding:
+    with no routed or shared contribution the output is the (BF16) residual
+    itself; residual and shared rows play symmetric roles; a zero residual
+    changes nothing; and a residual that cancels the shared row leaves the
+    routed sum alone."""
+    rng = np.random.default_rng(4)
+    T, k, d = 9, 4, 256
+    bf = lambda a: fp8.bf16_round(np.asarray(a, np.float32)).astype(np.float64)
+    yr, ys, res = bf(rng.standard_normal((T, k, d))), bf(rng.standard_normal((T, d))), bf(rng.standard_normal((T, d)))
+    w = rng.random((T, k)).astype(np.float32)
+    zero_y, zero_w, zero_s = np.zeros((T, k, d)), np.zeros((T, k), np.float32), np.zeros((T, d))
+    assert np.array_equal(layer.combine(zero_y, zero_w, zero_s, res), res)
+    assert np.array_equal(layer.combine(yr, w, ys, res), layer.combine(yr, w, res, ys))
+    assert np.array_equal(layer.combine(yr, w, ys, np.zeros((T, d))), layer.combine(yr, w, ys))
+    assert np.array_equal(layer.combine(yr, w, ys, -ys), layer.combine(yr, w, zero_s))
+    # one rounding of the exact sum, not a rounding per addend
+    exact = np.einsum("tk,tkd->td", w.astype(np.float64), yr) + ys + res
+    assert np.array_equal(layer.combine(yr, w, ys, res), fp8.bf16_round(exact))
+
 @pytest.mark.parametrize("k", [4, 8])
 def test_permute_combine_round_trip(k):
     """combine(permute(X), w = 1/k) == X bitwise (power-of-two weights)."""
