@@ -138,6 +138,13 @@ def timed_steps(layer, x, wg, b, W, steps):
     return (t1 - t0) * 1e3 / steps, stage_ms
 
 
+def gini(counts):
+    """Gini coefficient of the routed experts' row counts (0: equal loads)."""
+    c = np.sort(np.asarray(counts, np.float64))
+    n = len(c)
+    return float(2.0 * np.sum(np.arange(1, n + 1) * c) / (n * c.sum()) - (n + 1.0) / n) if c.sum() > 0 else 0.0
+
+
 def timed_graph(layer, x, wg, b, W, steps):
     """Milliseconds per forward replayed from a HIP graph (the same launches
     captured once; no launch gaps), bracketed by device synchronisations."""
@@ -281,6 +288,7 @@ def main():
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_of_fp8_peak": gemm_tflops / FP8_PEAK_TFLOPS,
         "expert_rows": {"max": int(counts.max()), "min": int(counts.min()),
+                        "max_over_mean": float(counts.max() / counts.mean()), "gini": gini(counts),
                         "experts_touched": touched},
         "weights_hbm_gbs": weight_bytes / (ms_per_step * 1e-3) / 1e9,
         "graph_replay": {"ms_per_step": graph_ms, "tokens_per_s": cfg.T / (graph_ms * 1e-3),

@@ -188,16 +188,20 @@ moe_status grouped_gemm_fp8_down(const uint8_t* h, const float* hs, const int32_
                                  const uint8_t* w2, const float* w2_s,
                                  uint16_t* y, void* stream);
 
-/* moe_combine — out[t] = BF16( sum_j w[t][j] * y[pos[t][j]] + y[shared_row0 + t] )
+/* moe_combine — out[t] = BF16( sum_j w[t][j] * y[pos[t][j]] + y[shared_row0 + t]
+ *                              + residual[t] )
  * (book chapter 7 "Selecting and combining experts"; chapter 15 "What combine
- * must do"), summed in FP32 in slot order.
+ * must do", which lists the residual path among what combine adds), summed in
+ * FP32 in slot order, then the shared row, then the residual, rounded once.
  *   y            [rows, d] BF16 expert outputs
  *   pos, w       [T, k] rows and gates of each token
  *   shared_row0  first shared-expert row (T*k), or -1 for none
- *   out          [T, d] BF16 */
+ *   residual     [T, d] BF16, or NULL for none (the layer passes none: its
+ *                output is the MoE branch)
+ *   out          [T, d] BF16 (may not alias y or residual) */
 moe_status moe_combine(const uint16_t* y, const int32_t* pos, const float* w,
                        int T, int k, int d, int32_t shared_row0,
-                       uint16_t* out, void* stream);
+                       const uint16_t* residual, uint16_t* out, void* stream);
 
 /* moe_bias_update — one step of the auxiliary-loss-free balancing controller
  * ("DeepSeek-V3: the recipe, and the interconnect that shaped it", section

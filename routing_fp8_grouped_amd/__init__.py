@@ -188,14 +188,17 @@ def grouped_gemm_fp8_down_e8m0(h, hs, offsets, w2, w2_s, y, stream=None):
     _gemm_down("grouped_gemm_fp8_down_e8m0", h, hs, offsets, w2, w2_s, y, stream)
 
 
-def moe_combine(y, pos, w, shared_row0, out, stream=None):
-    """out [T, d] = BF16(sum_j w[t, j] * y[pos[t, j]] + y[shared_row0 + t])."""
+def moe_combine(y, pos, w, shared_row0, out, stream=None, residual=None):
+    """out [T, d] = BF16(sum_j w[t, j] * y[pos[t, j]] + y[shared_row0 + t]
+    (+ residual[t] when given, a [T, d] BF16 tensor))."""
     _dev(y, torch.bfloat16, "y"); _dev(pos, torch.int32, "pos"); _dev(w, torch.float32, "w")
-    _dev(out, torch.bfloat16, "out")
+    _dev(out, torch.bfloat16, "out"); _dev(residual, torch.bfloat16, "residual")
     T, k = pos.shape
+    if residual is not None and tuple(residual.shape) != tuple(out.shape):
+        raise ValueError("residual must have the shape of out")
     lib = _lib.load()
     _lib.check("moe_combine", lib.moe_combine(_ptr(y), _ptr(pos), _ptr(w), T, k, y.shape[1],
-                                              shared_row0, _ptr(out), _stream(stream)))
+                                              shared_row0, _ptr(residual), _ptr(out), _stream(stream)))
 
 
 def moe_bias_update(offsets, bias, gamma, stream=None):

@@ -46,7 +46,7 @@ SIGNATURES = {
     "grouped_gemm_fp8_swiglu": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P, P, P, P]),
     "grouped_gemm_fp8_up": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P]),
     "grouped_gemm_fp8_down": (I, [P, P, P, I, I, I, I, P, P, P, P]),
-    "moe_combine": (I, [P, P, P, I, I, I, ctypes.c_int32, P, P]),
+    "moe_combine": (I, [P, P, P, I, I, I, ctypes.c_int32, P, P, P]),
     "moe_bias_update": (I, [P, I, ctypes.c_float, P, P]),
     "fp8_quant_1x128_pow2": (I, [P, I, I, P, P, P]),
     "fp8_quant_128x128_pow2": (I, [P, I, I, P, P, P]),

@@ -522,7 +522,7 @@ moe_status grouped_gemm_fp8_wgrad(const uint8_t* a_t, const float* a_ts, const u
 }
 
 moe_status moe_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k, int d,
-                       int32_t shared_row0, uint16_t* out, void* stream) {
+                       int32_t shared_row0, const uint16_t* residual, uint16_t* out, void* stream) {
   clear_error();
   REQUIRE(T >= 0, "T=%d is negative", T);
   REQUIRE(k >= 1 && k <= 16, "k=%d must be in [1, 16]", k);
@@ -534,7 +534,9 @@ moe_status moe_combine(const uint16_t* y, const int32_t* pos, const float* w, in
   REQUIRE_PTR4(pos);
   REQUIRE_PTR4(w);
   REQUIRE_PTR(out);
-  return hip_status(moe::launch_combine(y, pos, w, T, k, d, shared_row0, out,
+  REQUIRE(residual == nullptr || (reinterpret_cast<uintptr_t>(residual) & 15u) == 0,
+          "residual is not 16-byte aligned");
+  return hip_status(moe::launch_combine(y, pos, w, T, k, d, shared_row0, residual, out,
                                         static_cast<hipStream_t>(stream)),
                     "moe_combine launch");
 }

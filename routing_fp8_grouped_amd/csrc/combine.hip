@@ -6,8 +6,9 @@
 //
 // One workgroup per token; each thread owns 8 consecutive columns (16-byte
 // loads of every source row, one 16-byte store).  The sum is FP32 in slot
-// order, then the shared row, so the result is deterministic.  HBM-bound:
-// (k + 1) BF16 rows read and one written per token.
+// order, then the shared row, then the optional residual row (chapter 15
+// lists the residual path among what combine adds), so the result is
+// deterministic.  HBM-bound: (k + 1) BF16 rows read and one written per token.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,6 +18,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       const int32_t* __restrict__ pos,
                                                       const float* __restrict__ w, int k, int d,
                                                       int rows, int shared_row0,
+                                                      const uint16_t* __restrict__ residual,
                                                       uint16_t* __restrict__ out) {
   __shared__ int s_pos[16];
   __shared__ float s_w[16];
@@ -52,6 +54,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
         acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
       }
     }
+    if (residual) {
+      const uint4 v = *reinterpret_cast<const uint4*>(residual + (size_t)t * d + c * 8);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
+        acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
+      }
+    }
     uint4 o;
     o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
     o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
@@ -62,10 +73,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 }
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k,
-                          int d, int shared_row0, uint16_t* out, hipStream_t stream) {
+                          int d, int shared_row0, const uint16_t* residual, uint16_t* out,
+                          hipStream_t stream) {
   const int rows = T * k + (shared_row0 >= 0 ? T : 0);
   hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, stream, y, pos, w, k, d,
-                     shared_row0 >= 0 ? shared_row0 + T : rows, shared_row0, out);
+                     shared_row0 >= 0 ? shared_row0 + T : rows, shared_row0, residual, out);
   return hipGetLastError();
 }
 

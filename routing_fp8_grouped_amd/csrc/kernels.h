@@ -71,6 +71,7 @@ hipError_t launch_wgrad(const uint8_t* A, const float* sA, const uint8_t* B, con
                         hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int k,
-                          int d, int shared_row0, uint16_t* out, hipStream_t stream);
+                          int d, int shared_row0, const uint16_t* residual, uint16_t* out,
+                          hipStream_t stream);
 
 }  // namespace moe

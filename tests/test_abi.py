@@ -167,11 +167,12 @@ def test_gemm_validation(lib):
 
 
 def test_combine_validation(lib):
-    assert lib.moe_combine(A, A, A, 10, 0, 256, 80, A, None) == 1
-    assert lib.moe_combine(A, A, A, 10, 8, 100, 80, A, None) == 1
-    assert lib.moe_combine(A, A, A, 10, 8, 256, -2, A, None) == 1
-    assert lib.moe_combine(A, None, A, 10, 8, 256, 80, A, None) == 1 and "pos is NULL" in last(lib)
-    assert lib.moe_combine(None, None, None, 0, 8, 256, 0, None, None) == 0
+    assert lib.moe_combine(A, A, A, 10, 0, 256, 80, None, A, None) == 1
+    assert lib.moe_combine(A, A, A, 10, 8, 100, 80, None, A, None) == 1
+    assert lib.moe_combine(A, A, A, 10, 8, 256, -2, None, A, None) == 1
+    assert lib.moe_combine(A, None, A, 10, 8, 256, 80, None, A, None) == 1 and "pos is NULL" in last(lib)
+    assert lib.moe_combine(A, A, A, 10, 8, 256, 80, MIS, A, None) == 1 and "residual" in last(lib)
+    assert lib.moe_combine(None, None, None, 0, 8, 256, 0, None, None, None) == 0
 
 
 def test_bias_update_validation(lib):

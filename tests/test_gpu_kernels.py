@@ -150,12 +150,13 @@ def test_route_parity(T, d, E, G, M, k, rho):
     (70, 256, 256, 16, 4, 16), (65, 128, 40, 8, 2, 4)])
 def test_route_ws_matches_single_kernel(T, d, E, G, M, k):
     """The two-kernel router (workspace) returns moe_route's result bit for bit:
-    the same logit arithmetic, the same selection code."""
+    the same logit arithmetic, the same selection code (with a bias, and
+    without one on odd T)."""
     log(f"route_ws T={T} d={d} E={E} G={G} M={M} k={k}")
     rng = np.random.default_rng(T + 7 * E + d)
     x = bf16_tensor(rng.standard_normal((T, d))).to(DEV)
     wg = bf16_tensor(rng.standard_normal((E, d)) / np.sqrt(d)).to(DEV)
-    b = torch.from_numpy(rng.uniform(-0.05, 0.05, E).astype(np.float32)).to(DEV)
+    b = torch.from_numpy(rng.uniform(-0.05, 0.05, E).astype(np.float32)).to(DEV) if T % 2 == 0 else None
     out = []
     for ws in (None, torch.empty(max(16, moe.moe_route_workspace_bytes(T, E)), dtype=torch.uint8, device=DEV)):
         idx = torch.full((T, k), -1, dtype=torch.int32, device=DEV)
@@ -292,8 +293,9 @@ def test_gemm_parity(counts, d, f, gather):
         f"rows above 5e-3 (within the ambiguity allowance): {n_allow}/{rows}")
 
 
-def test_combine_parity():
-    log("combine")
+@pytest.mark.parametrize("with_residual", [False, True])
+def test_combine_parity(with_residual):
+    log(f"combine (residual: {with_residual})")
     rng = np.random.default_rng(5)
     T, k, E, d = 300, 8, 64, 512
     idx = random_idx(rng, T, E, k)
@@ -302,16 +304,21 @@ def test_combine_parity():
     y = bf16_tensor(rng.standard_normal((rows, d)))
     w = rng.random((T, k)).astype(np.float32)
     w = (2.5 * w / w.sum(1, keepdims=True)).astype(np.float32)
+    res = bf16_tensor(rng.standard_normal((T, d)) * 3.0) if with_residual else None
     out = torch.empty(T, d, dtype=torch.bfloat16, device=DEV)
-    moe.moe_combine(y.to(DEV), torch.from_numpy(pos).to(DEV), torch.from_numpy(w).to(DEV), T * k, out)
+    moe.moe_combine(y.to(DEV), torch.from_numpy(pos).to(DEV), torch.from_numpy(w).to(DEV), T * k, out,
+                    residual=None if res is None else res.to(DEV))
     torch.cuda.synchronize()
     yn = y.float().numpy()
-    ref = olayer.combine(yn[pos.astype(np.int64)], w, yn[T * k:])
+    rn = None if res is None else res.float().numpy()
+    ref = olayer.combine(yn[pos.astype(np.int64)], w, yn[T * k:], rn)
     got = to_np(out)
     # FP32 sum in slot order vs the float64 sum: one BF16 step where the two
     # land on different sides of a rounding boundary, plus the FP32 sum's own
     # error where the terms cancel
     diff = np.abs(got.astype(np.float64) - ref)
     terms = np.einsum("tk,tkd->td", np.abs(w), np.abs(yn[pos.astype(np.int64)])) + np.abs(yn[T * k:])
+    if rn is not None:
+        terms += np.abs(rn)
     assert np.all(diff <= np.abs(ref) * 2.0 ** -7 + 16 * 2.0 ** -24 * terms)
     assert np.mean(got != ref) < 0.01
