@@ -124,11 +124,13 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, const int32_t* __
   t.g = a;
   t.n = rem / msb;
   const int m = sb * SUPER_M + (rem - t.n * msb);
-  // first GEMM: the group's rows split evenly over its mt tiles (multiples of
-  // 16), so the tiles sharing a weight panel take equally long and stay
-  // together in L2
+  // the group's rows split evenly over its mt tiles (multiples of 16), so the
+  // tiles sharing a weight panel take equally long and stay together in L2
+  // (a short remainder tile would run ahead and make the others fetch the
+  // panel again).  Used by the first GEMM and by any K of 32 blocks or more;
+  // with the second GEMM's 16 blocks the drift is too short to matter.
   const int R = offsets[a + 1] - offsets[a];
-  const int rpt = p.h ? min(BM, ((R + mt - 1) / mt + 15) / 16 * 16) : BM;
+  const int rpt = (p.h || p.K >= 32 * BK) ? min(BM, ((R + mt - 1) / mt + 15) / 16 * 16) : BM;
   t.row0 = offsets[a] + m * rpt;
   // rows past total_rows (only possible with malformed offsets) are never touched
   t.rows_valid = max(0, min(rpt, min(offsets[a + 1], p.total_rows) - t.row0));
