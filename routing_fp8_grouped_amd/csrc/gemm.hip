@@ -17,17 +17,23 @@
 // a single MFMA spans exactly one scale block.)
 //
 // Per workgroup: 512 threads = 8 waves, two per SIMD, in a 4 x 2 grid.  Wave
-// (wm, wn) owns rows wm*64 .. +63 and weight-tile rows wn*128 .. +127 (in stage
-// 1: wn = 0 the gate rows, wn = 1 the up rows of the same h columns), i.e.
-// 4 x 8 MFMA sub-tiles and one weight scale block per K block.  With two waves
-// per SIMD the promotion FMAs of one wave issue while the other wave's MFMAs
-// run; within a wave each promotion trails its MFMA by two instructions.
+// (wm, wn) owns rows wm*64 .. +63 and 128 weight-tile rows, i.e. 4 x 8 MFMA
+// sub-tiles: in stage 1 the gate rows wn*64 .. +63 and the up rows of the same
+// 64 h columns (so SiLU(G) * U is formed in registers and only the row amax of
+// the 1x128 requantisation crosses waves), in stage 2 rows wn*128 .. +127.
+// The weight fragment is the MFMA's first operand, so each lane holds four
+// consecutive output columns of one row, and the promotion factor (row scale x
+// weight-block scale) is one register per lane and sub-tile row block.  With
+// two waves per SIMD the promotion FMAs of one wave issue while the other
+// wave's MFMAs run; within a wave each promotion trails its MFMA by two
+// instructions.
 //
 // Operands stream HBM -> LDS through a two-stage ring filled by direct
 // global->LDS loads (no VGPR round trip).  Each K block has one barrier, placed
 // after the wave's last LDS read of the block: past it the block's stage is
 // refilled with the block two ahead, and the first fragments of the next block
-// are read while the last MFMAs of this block run.
+// are read while the last MFMAs of this block run.  Stage 1's epilogue needs no
+// LDS staging, so the ring keeps loading the next tile while it runs.
 //
 // Power-of-two variant (E8M0): when every activation, weight and H scale is a
 // power of two (the quantisers' power-of-two rule), the scales go into the
@@ -162,6 +168,15 @@ __device__ __forceinline__ int weight_row(const GemmArgs& p, int n, int rr) {
   return n * BN + rr;
 }
 
+// LDS weight-tile row of sub-tile column ns of wave column wn.  In stage 1 a
+// wave takes 64 gate rows (ns 0..3) and the matching 64 up rows (ns 4..7), so
+// SiLU(G) * U is formed in registers; in stage 2 it takes 128 consecutive rows.
+template <bool SWIGLU>
+__device__ __forceinline__ int brow(int wn, int ns) {
+  if (SWIGLU) return (ns < 4 ? 0 : 128) + wn * 64 + (ns & 3) * 16;
+  return wn * 128 + ns * 16;
+}
+
 // Gather indices of a tile's 256 rows, loaded into an LDS table one tile ahead
 // (waves 0..3, lane l: tile row 64 w + l), so no register waits on them.
 __device__ __forceinline__ void dma_tile_rows(const GemmArgs& p, const Tile& t, int wave, int lane,
@@ -230,7 +245,6 @@ __device__ __forceinline__ v8i frag(const unsigned char* T, int r, int g16) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// SiLU(g) * u in FP32.
 // SiLU(g) * u in FP32: exp(-g) to within an ulp, the quotient by the hardware
 // reciprocal (1 ulp); a few ulp from the exactly rounded value.
 __device__ __forceinline__ float swiglu(float g, float u) {
@@ -250,130 +264,79 @@ __device__ __forceinline__ float div_by(float x, float s, float r) {
   return fmaf(fmaf(-s, q, x), r, q);
 }
 
-// ---- epilogues: one 64 x 128 block per wave, written through the wave's own
-// part of the finished ring stage E, 32 rows per round ----
+// ---- epilogues ----
+// With the weight fragment as the MFMA's first operand, lane (g16, r16) holds
+// in acc[ms][ns] row ms*16 + r16 of the wave's 64 rows and the 4 consecutive
+// columns brow(wn, ns) + 4*g16 + e of the weight tile.
 
-// Stage 1.  Wave (wm, 0) holds g, wave (wm, 1) holds u for the same 64 x 128
-// block of h.  Column WN finishes h columns 64 WN .. 64 WN + 63: it sends the
-// other half to its partner and receives the partner's half of its own.  h
-// replaces g (WN = 0) or u (WN = 1) in the accumulator.  Then the 1x128 amax
-// is combined across the pair through smAmax, and the E4M3 codes are staged
-// for 16-byte stores.
-template <int WN, bool POW2>
-__device__ __forceinline__ void epilogue_swiglu(const GemmArgs& p, const Tile& cur, v4f (&acc)[4][8],
-                                                unsigned char* E, float (*smAmax)[BM], int wave,
-                                                int wm, int lane) {
-  const int g16 = lane >> 4, r16 = lane & 15;
-  float* X = reinterpret_cast<float*>(E);
-  float* mine = X + wave * 2048;
-  const float* other = X + (wave ^ 1) * 2048;
-  const int nhs = p.f / 128;
-  constexpr int SEND = WN == 0 ? 4 : 0;   // sub-tile columns sent to the partner
-  constexpr int KEEP = WN == 0 ? 0 : 4;   // sub-tile columns finished here
-  if (p.gu) {
-    // the SwiGLU input for the backward: this wave's 64 rows x 128 columns of
-    // G (WN = 0) or U (WN = 1) are exactly 1x128 tiles; quantised with the
-    // forward's rule, staged through the wave's own LDS region, stored by rows
-    unsigned char* Q = reinterpret_cast<unsigned char*>(mine);
-    const int ngs = 2 * nhs;
+// 1x128 quantisation of the 64 x 64 block acc[.][j0 .. j0+3] of each wave, whose
+// partner wave (wn ^ 1) holds the other 64 columns of the same 1x128 tiles:
+// row amax over the lane's 16 values, the 4 lanes of the row and, through
+// smAmax, the partner; then the E4M3 codes, 4 per 32-bit store.  `out` points
+// at the wave's first column of tile row 0, rows `ld` bytes apart; the scale of
+// tile row r goes to sout[(row0 + r) * sld] (written by wave column 0).
+template <bool POW2>
+__device__ __forceinline__ void quantise_rows(const v4f (&acc)[4][8], int j0, float (*smAmax)[BM], int wm,
+                                              int wn, int g16, int r16, const Tile& cur, uint8_t* out,
+                                              size_t ld, float* sout, int sld) {
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
+  for (int ms = 0; ms < 4; ++ms) {
+    float a = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float a = 0.0f;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int ns = 0; ns < 8; ++ns) a = fmaxf(a, fabsf(acc[ms][ns][e]));
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
-        const float sc = tile_scale<POW2>(a);
-        const float rs = recip(sc);
-        const int rt = wm * 64 + ms * 16 + g16 * 4 + e;
-        if (r16 == 0 && rt < cur.rows_valid) p.gus[(size_t)(cur.row0 + rt) * ngs + WN * nhs + cur.n] = sc;
-#pragma unroll
-        for (int ns = 0; ns < 8; ++ns)
-          Q[(ms * 16 + g16 * 4 + e) * 128 + ns * 16 + r16] =
-              (unsigned char)(f32x2_to_e4m3(div_by(acc[ms][ns][e], sc, rs), 0.0f) & 0xFFu);
-      }
-    wave_sync_lds();
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int idx = it * 64 + lane;
-      const int rl = idx >> 3, cq = idx & 7;
-      const int rt = wm * 64 + rl;
-      const uint4 v = *reinterpret_cast<const uint4*>(Q + rl * 128 + cq * 16);
-      if (rt < cur.rows_valid)
-        *reinterpret_cast<uint4*>(p.gu + (size_t)(cur.row0 + rt) * 2 * p.f + WN * p.f + cur.n * 128 + cq * 16) = v;
-    }
-    wave_sync_lds();
+      for (int e = 0; e < 4; ++e) a = fmaxf(a, fabsf(acc[ms][j0 + j][e]));
+    a = fmaxf(a, __shfl_xor(a, 16));
+    a = fmaxf(a, __shfl_xor(a, 32));
+    if (g16 == 0) smAmax[wn][wm * 64 + ms * 16 + r16] = a;
   }
+  lds_barrier();
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    __builtin_amdgcn_sched_barrier(0);
+  for (int ms = 0; ms < 4; ++ms) {
+    const int rt = wm * 64 + ms * 16 + r16;
+    const float sc = tile_scale<POW2>(fmaxf(smAmax[0][rt], smAmax[1][rt]));
+    const float rs = recip(sc);
+    const bool ok = rt < cur.rows_valid;
+    if (wn == 0 && g16 == 0 && ok) sout[(size_t)(cur.row0 + rt) * sld] = sc;
 #pragma unroll
-    for (int msl = 0; msl < 2; ++msl)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          mine[((msl * 4 + j) * 4 + e) * 64 + lane] = acc[2 * r + msl][SEND + j][e];
-    lds_barrier();
-    float amax[2][4];
-#pragma unroll
-    for (int msl = 0; msl < 2; ++msl) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) amax[msl][e] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = other[((msl * 4 + j) * 4 + e) * 64 + lane];
-          const float mv = acc[2 * r + msl][KEEP + j][e];
-          const float h = WN == 0 ? swiglu(mv, v) : swiglu(v, mv);
-          acc[2 * r + msl][KEEP + j][e] = h;
-          amax[msl][e] = fmaxf(amax[msl][e], fabsf(h));
-        }
+    for (int j = 0; j < 4; ++j) {
+      const v4f v = acc[ms][j0 + j];
+      const uint32_t q = f32x4_to_e4m3(div_by(v[0], sc, rs), div_by(v[1], sc, rs), div_by(v[2], sc, rs),
+                                       div_by(v[3], sc, rs));
+      if (ok) *reinterpret_cast<uint32_t*>(out + (size_t)(cur.row0 + rt) * ld + j * 16) = q;
     }
-#pragma unroll
-    for (int msl = 0; msl < 2; ++msl)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v = amax[msl][e];
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-        if (r16 == 0) smAmax[WN][wm * 64 + (2 * r + msl) * 16 + g16 * 4 + e] = v;
-      }
-    lds_barrier();   // amax of both halves visible; the partner is done with `mine`
-    unsigned char* Q = reinterpret_cast<unsigned char*>(mine);   // 32 rows x 64 bytes
-#pragma unroll
-    for (int msl = 0; msl < 2; ++msl)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rt = wm * 64 + (2 * r + msl) * 16 + g16 * 4 + e;
-        const float sc = tile_scale<POW2>(fmaxf(smAmax[0][rt], smAmax[1][rt]));
-        const float rs = recip(sc);
-        if (WN == 0 && r16 == 0 && rt < cur.rows_valid) p.hs[(size_t)(cur.row0 + rt) * nhs + cur.n] = sc;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t q = f32x2_to_e4m3(div_by(acc[2 * r + msl][KEEP + j][e], sc, rs), 0.0f) & 0xFFu;
-          Q[(msl * 16 + g16 * 4 + e) * 64 + j * 16 + r16] = (unsigned char)q;
-        }
-      }
-    wave_sync_lds();
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int idx = it * 64 + lane;
-      const int rl = idx >> 2, cq = idx & 3;
-      const int rt = wm * 64 + 2 * r * 16 + rl;
-      const uint4 v = *reinterpret_cast<const uint4*>(Q + rl * 64 + cq * 16);
-      if (rt < cur.rows_valid)
-        *reinterpret_cast<uint4*>(p.h + (size_t)(cur.row0 + rt) * p.f + cur.n * 128 + WN * 64 + cq * 16) = v;
-    }
-    wave_sync_lds();
   }
+  lds_barrier();   // every wave has read smAmax before it is written again
 }
 
-// Stage 2: BF16 rows, 32 rows x 128 columns per round.
+// Stage 1: the optional FP8 cache of G and U (1x128 tiles, the forward's
+// rule), then h = SiLU(G) * U in place of G and its 1x128 requantisation.
+// The wave's columns of the tile's 128-wide slice of f are wn*64 .. +63.
+template <bool POW2>
+__device__ __forceinline__ void epilogue_swiglu(const GemmArgs& p, const Tile& cur, v4f (&acc)[4][8],
+                                                float (*smAmax)[BM], int wm, int wn, int lane) {
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int nhs = p.f / 128;
+  const size_t col = (size_t)cur.n * 128 + wn * 64 + 4 * g16;
+  if (p.gu) {
+    quantise_rows<POW2>(acc, 0, smAmax, wm, wn, g16, r16, cur, p.gu + col, 2 * (size_t)p.f, p.gus + cur.n,
+                        2 * nhs);
+    quantise_rows<POW2>(acc, 4, smAmax, wm, wn, g16, r16, cur, p.gu + p.f + col, 2 * (size_t)p.f,
+                        p.gus + nhs + cur.n, 2 * nhs);
+  }
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[ms][j][e] = swiglu(acc[ms][j][e], acc[ms][4 + j][e]);
+  quantise_rows<POW2>(acc, 0, smAmax, wm, wn, g16, r16, cur, p.h + col, (size_t)p.f, p.hs + cur.n, nhs);
+}
+
+// Stage 2: BF16 rows staged through the wave's part of the finished ring stage
+// E, 32 rows x 128 columns per round; the 16-byte chunk c of staging row r sits
+// at c ^ (r & 15), so both the 8-byte writes and the 16-byte reads are free of
+// bank conflicts.
 __device__ __forceinline__ void epilogue_bf16(const GemmArgs& p, const Tile& cur, v4f (&acc)[4][8],
                                               unsigned char* E, int wave, int wm, int wn, int lane) {
   const int g16 = lane >> 4, r16 = lane & 15;
@@ -386,10 +349,15 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& p, const Tile& cur
 #pragma unroll
     for (int msl = 0; msl < 2; ++msl)
 #pragma unroll
-      for (int ns = 0; ns < 8; ++ns)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          X16[(msl * 16 + g16 * 4 + e) * 128 + ns * 16 + r16] = f32_to_bf16(acc[2 * r + msl][ns][e]);
+      for (int ns = 0; ns < 8; ++ns) {
+        const int row = msl * 16 + r16;
+        const int ch = (ns * 2 + (g16 >> 1)) ^ r16;
+        const v4f v = acc[2 * r + msl][ns];
+        uint2 w;
+        w.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        w.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<uint2*>(X16 + row * 128 + ch * 8 + (g16 & 1) * 4) = w;
+      }
     wave_sync_lds();
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
@@ -397,7 +365,7 @@ __device__ __forceinline__ void epilogue_bf16(const GemmArgs& p, const Tile& cur
       const int idx = it * 64 + lane;
       const int rl = idx >> 4, cq = idx & 15;
       const int rt = wm * 64 + 2 * r * 16 + rl;
-      const uint4 v = *reinterpret_cast<const uint4*>(X16 + rl * 128 + cq * 8);
+      const uint4 v = *reinterpret_cast<const uint4*>(X16 + rl * 128 + ((cq ^ (rl & 15)) * 8));
       if (rt < cur.rows_valid)
         *reinterpret_cast<uint4*>(p.y + (size_t)(cur.row0 + rt) * p.N + col0 + cq * 8) = v;
     }
@@ -447,41 +415,42 @@ struct Loader {
 struct Frags {
   v8i af[4];       // activation fragments of the block (rows ms*16 .. +15)
   v8i bq[2];       // weight fragments, column ns in slot ns & 1
-  float cs[4][4];  // activation scale x weight scale of this lane's 16 rows
-  int ea[4];       // E8M0 variant: scale code of this lane's A row of fragment ms
-  int eb;          // E8M0 variant: scale code of the wave's weight block
+  float cs[2][4];  // activation scale of this lane's row of fragment ms x weight scale ([1]: up rows)
+  int ea[4];       // E8M0 variant: scale code of this lane's activation row of fragment ms
+  int eb[2];       // E8M0 variant: scale code of the wave's weight block ([1]: up rows)
 };
 
-template <bool E8M0>
-__device__ __forceinline__ void load_scales(Frags& F, const unsigned char* stage, int wm, int wn, int g16,
-                                            int r16) {
+template <bool SWIGLU, bool E8M0>
+__device__ __forceinline__ void load_scales(Frags& F, const unsigned char* stage, int wm, int wn, int r16) {
   const unsigned char* B_ = stage + ST_A;
   if (E8M0) {
     const uint32_t* SA_ = reinterpret_cast<const uint32_t*>(B_ + ST_B);
-    F.eb = (int)(reinterpret_cast<const uint32_t*>(B_ + ST_B + ST_SA)[wn] >> 23);
+    const uint32_t* SW_ = reinterpret_cast<const uint32_t*>(B_ + ST_B + ST_SA);
+    F.eb[0] = (int)(SW_[SWIGLU ? 0 : wn] >> 23);
+    if (SWIGLU) F.eb[1] = (int)(SW_[1] >> 23);
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) F.ea[ms] = (int)(SA_[wm * 64 + ms * 16 + r16] >> 23);
     return;
   }
   const float* SA_ = reinterpret_cast<const float*>(B_ + ST_B);
-  const float sw = reinterpret_cast<const float*>(B_ + ST_B + ST_SA)[wn];
+  const float* SW_ = reinterpret_cast<const float*>(B_ + ST_B + ST_SA);
+  const float s0 = SW_[SWIGLU ? 0 : wn];
+  const float s1 = SW_[1];
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms) {
-    const float4 s4 = *reinterpret_cast<const float4*>(&SA_[wm * 64 + ms * 16 + g16 * 4]);
-    F.cs[ms][0] = s4.x * sw;
-    F.cs[ms][1] = s4.y * sw;
-    F.cs[ms][2] = s4.z * sw;
-    F.cs[ms][3] = s4.w * sw;
+    const float sa = SA_[wm * 64 + ms * 16 + r16];
+    F.cs[0][ms] = sa * s0;
+    if (SWIGLU) F.cs[1][ms] = sa * s1;
   }
 }
 
-template <bool E8M0>
+template <bool SWIGLU, bool E8M0>
 __device__ __forceinline__ void load_first(Frags& F, const unsigned char* stage, int wm, int wn, int g16,
                                            int r16) {
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms) F.af[ms] = frag(stage, wm * 64 + ms * 16 + r16, g16);
-  F.bq[0] = frag(stage + ST_A, wn * 128 + r16, g16);
-  load_scales<E8M0>(F, stage, wm, wn, g16, r16);
+  F.bq[0] = frag(stage + ST_A, brow<SWIGLU>(wn, 0) + r16, g16);
+  load_scales<SWIGLU, E8M0>(F, stage, wm, wn, r16);
 }
 
 // One K block on stage `cur`: MFMA i = (ns, ms) in ns-major order, each
@@ -512,31 +481,32 @@ __device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGL
     // columns (an empty asm with a memory clobber pins them in order)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    if (ns < 7) F.bq[(ns + 1) & 1] = frag(Bc, wn * 128 + (ns + 1) * 16 + r16, g16);
+    if (ns < 7) F.bq[(ns + 1) & 1] = frag(Bc, brow<SWIGLU>(wn, ns + 1) + r16, g16);
     if (ns == 7) {
       ring_barrier();
       if (!LAST) {
         if (ld.more) ld.issue(cur);
-        F.bq[0] = frag(nxt + ST_A, wn * 128 + r16, g16);
+        F.bq[0] = frag(nxt + ST_A, brow<SWIGLU>(wn, 0) + r16, g16);
       }
     }
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) {
       const int i = ns * 4 + ms;
       if (E8M0) {
-        acc[ms][ns] = mfma_fp8_16x16x128_scaled(F.af[ms], F.bq[ns & 1], acc[ms][ns], F.ea[ms], F.eb);
+        acc[ms][ns] = mfma_fp8_16x16x128_scaled(F.bq[ns & 1], F.af[ms], acc[ms][ns],
+                                                F.eb[SWIGLU ? (ns >> 2) : 0], F.ea[ms]);
         if (i >= 1) {
           const int pi = i - 1;
           asm volatile("" : "+v"(acc[pi & 3][pi >> 2]));
         }
       } else {
-        part[i & 1] = mfma_fp8_16x16x128(F.af[ms], F.bq[ns & 1], v4f{0.f, 0.f, 0.f, 0.f});
+        part[i & 1] = mfma_fp8_16x16x128(F.bq[ns & 1], F.af[ms], v4f{0.f, 0.f, 0.f, 0.f});
       }
       if (!E8M0 && i >= 1) {
         const int pi = i - 1, pms = pi & 3, pns = pi >> 2;
+        const float c = F.cs[SWIGLU ? (pns >> 2) : 0][pms];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[pms][pns][e] = fmaf(part[pi & 1][e], F.cs[pms][e], acc[pms][pns][e]);
+        for (int e = 0; e < 4; ++e) acc[pms][pns][e] = fmaf(part[pi & 1][e], c, acc[pms][pns][e]);
         // pins the promotion (and so the MFMAs before it) at this point: the
         // compiler would otherwise sink the block's arithmetic past the ring
         // barrier and hold every weight fragment at once
@@ -552,8 +522,8 @@ __device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGL
   }
   if (!E8M0)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[3][7][e] = fmaf(part[1][e], F.cs[3][e], acc[3][7][e]);
-  if (!LAST) load_scales<E8M0>(F, nxt, wm, wn, g16, r16);
+    for (int e = 0; e < 4; ++e) acc[3][7][e] = fmaf(part[1][e], F.cs[SWIGLU ? 1 : 0][3], acc[3][7][e]);
+  if (!LAST) load_scales<SWIGLU, E8M0>(F, nxt, wm, wn, r16);
 }
 
 template <bool SWIGLU, bool E8M0>
@@ -622,26 +592,27 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_kernel(GemmArgs p,
       for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = v4f{0.f, 0.f, 0.f, 0.f};
     // rows wm*64 .. +63 hold data (uniform per wave)
     const bool active = wm * 64 < cur.rows_valid;
-    if (active) load_first<E8M0>(F, sm + S * STG, wm, wn, g16, r16);
+    if (active) load_first<SWIGLU, E8M0>(F, sm + S * STG, wm, wn, g16, r16);
     for (int kb = 0; kb < KB - 1; ++kb) {
       k_block<SWIGLU, false, E8M0>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16, active);
       S ^= 1;
     }
     k_block<SWIGLU, true, E8M0>(acc, F, ld, sm + S * STG, sm + (S ^ 1) * STG, wm, wn, g16, r16, active);
 
-    // ---- epilogue, through stage S (every wave has finished reading it: the
-    // ring barrier of the last block followed the last read) ----
+    // ---- epilogue.  Every wave has finished reading stage S (the ring
+    // barrier of the last block followed the last read); the next tile's
+    // first block is in stage S ^ 1 (landed at that barrier) ----
     unsigned char* E = sm + S * STG;
     if (SWIGLU) {
-      if (wn == 0) epilogue_swiglu<0, E8M0>(p, cur, acc, E, smAmax, wave, wm, lane);
-      else epilogue_swiglu<1, E8M0>(p, cur, acc, E, smAmax, wave, wm, lane);
+      // the epilogue works in registers: stage S is refilled before it
+      if (ld.more) ld.issue(E);
+      epilogue_swiglu<E8M0>(p, cur, acc, smAmax, wm, wn, lane);
     } else {
+      // staged through stage S, refilled once every wave is done with it
       epilogue_bf16(p, cur, acc, E, wave, wm, wn, lane);
+      lds_barrier();
+      if (ld.more) ld.issue(E);
     }
-    // stage S is free again once every wave has finished its epilogue; the
-    // next tile's first block is in stage S ^ 1 (landed at the last barrier)
-    lds_barrier();
-    if (ld.more) ld.issue(E);
     S ^= 1;
   }
 }
