@@ -25,8 +25,9 @@
 // consecutive output columns of one row, and the promotion factor (row scale x
 // weight-block scale) is one register per lane and sub-tile row block.  With
 // two waves per SIMD the promotion FMAs of one wave issue while the other
-// wave's MFMAs run; within a wave each promotion trails its MFMA by two
-// instructions.
+// wave's MFMAs run; within a wave each promotion follows two MFMAs after its
+// own (one in the second GEMM, whose register budget is tighter), so its FMAs
+// do not wait for the MFMA result.
 //
 // Operands stream HBM -> LDS through a two-stage ring filled by direct
 // global->LDS loads (no VGPR round trip).  Each K block has one barrier, placed
@@ -474,7 +475,10 @@ __device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGL
     return;
   }
   const unsigned char* Bc = cur + ST_A;
-  v4f part[2];
+  // each partial sum is promoted PD MFMAs after its own, so the FMAs never
+  // wait for an MFMA in flight
+  constexpr int PD = SWIGLU ? 2 : 1;
+  v4f part[PD + 1];
 #pragma unroll
   for (int ns = 0; ns < 8; ++ns) {
     // the register budget holds two weight fragments: no LDS read moves across
@@ -500,13 +504,13 @@ __device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGL
           asm volatile("" : "+v"(acc[pi & 3][pi >> 2]));
         }
       } else {
-        part[i & 1] = mfma_fp8_16x16x128(F.bq[ns & 1], F.af[ms], v4f{0.f, 0.f, 0.f, 0.f});
+        part[i % (PD + 1)] = mfma_fp8_16x16x128(F.bq[ns & 1], F.af[ms], v4f{0.f, 0.f, 0.f, 0.f});
       }
-      if (!E8M0 && i >= 1) {
-        const int pi = i - 1, pms = pi & 3, pns = pi >> 2;
+      if (!E8M0 && i >= PD) {
+        const int pi = i - PD, pms = pi & 3, pns = pi >> 2;
         const float c = F.cs[SWIGLU ? (pns >> 2) : 0][pms];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[pms][pns][e] = fmaf(part[pi & 1][e], c, acc[pms][pns][e]);
+        for (int e = 0; e < 4; ++e) acc[pms][pns][e] = fmaf(part[pi % (PD + 1)][e], c, acc[pms][pns][e]);
         // pins the promotion (and so the MFMAs before it) at this point: the
         // compiler would otherwise sink the block's arithmetic past the ring
         // barrier and hold every weight fragment at once
@@ -522,7 +526,12 @@ __device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGL
   }
   if (!E8M0)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[3][7][e] = fmaf(part[1][e], F.cs[SWIGLU ? 1 : 0][3], acc[3][7][e]);
+    for (int pi = 32 - PD; pi < 32; ++pi) {
+      const int pms = pi & 3, pns = pi >> 2;
+      const float c = F.cs[SWIGLU ? (pns >> 2) : 0][pms];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[pms][pns][e] = fmaf(part[pi % (PD + 1)][e], c, acc[pms][pns][e]);
+    }
   if (!LAST) load_scales<SWIGLU, E8M0>(F, nxt, wm, wn, r16);
 }
 
