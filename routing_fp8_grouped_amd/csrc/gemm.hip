@@ -33,8 +33,8 @@
 // global->LDS loads (no VGPR round trip).  Each K block has one barrier, placed
 // after the wave's last LDS read of the block: past it the block's stage is
 // refilled with the block two ahead, and the first fragments of the next block
-// are read while the last MFMAs of this block run.  Stage 1's epilogue needs no
-// LDS staging, so the ring keeps loading the next tile while it runs.
+// are read while the last MFMAs of this block run.  The epilogues need no LDS
+// staging, so the ring keeps loading the next tile while they run.
 //
 // Power-of-two variant (E8M0): when every activation, weight and H scale is a
 // power of two (the quantisers' power-of-two rule), the scales go into the
@@ -93,12 +93,6 @@ constexpr int ST_B = BN * BK;                   // weight tile, 32 KB
 constexpr int ST_SA = BM * 4;                   // activation scales of the 256 rows
 constexpr int ST_SW = 256;                      // weight scales: [0] wave column 0, [1] column 1
 constexpr int STG = ST_A + ST_B + ST_SA + ST_SW;
-
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Barrier for LDS data only: waits for this wave's LDS operations, not for the
 // direct loads in flight.
@@ -334,43 +328,31 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& p, const Tile& c
   quantise_rows<POW2>(acc, 0, smAmax, wm, wn, g16, r16, cur, p.h + col, (size_t)p.f, p.hs + cur.n, nhs);
 }
 
-// Stage 2: BF16 rows staged through the wave's part of the finished ring stage
-// E, 32 rows x 128 columns per round; the 16-byte chunk c of staging row r sits
-// at c ^ (r & 15), so both the 8-byte writes and the 16-byte reads are free of
-// bank conflicts.
-__device__ __forceinline__ void epilogue_bf16(const GemmArgs& p, const Tile& cur, v4f (&acc)[4][8],
-                                              unsigned char* E, int wave, int wm, int wn, int lane) {
+// Stage 2: BF16 from registers.  Lane pairs (l, l + 16) trade halves with
+// v_permlane16_swap so that each lane holds 8 consecutive columns: sub-tile
+// column ns in the even 16-lane rows, ns + 1 in the odd ones.  Each store
+// then writes 16 bytes per lane and 64 contiguous bytes per row.
+__device__ __forceinline__ void epilogue_bf16(const GemmArgs& p, const Tile& cur, v4f (&acc)[4][8], int wm,
+                                              int wn, int lane) {
   const int g16 = lane >> 4, r16 = lane & 15;
   const int col0 = cur.n * BN + wn * 128;
   if (col0 >= p.N) return;
-  uint16_t* X16 = reinterpret_cast<uint16_t*>(E) + wave * 4096;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    __builtin_amdgcn_sched_barrier(0);
+  for (int ms = 0; ms < 4; ++ms) {
+    const int rt = wm * 64 + ms * 16 + r16;
+    uint16_t* yr = p.y + (size_t)(cur.row0 + rt) * p.N + col0 + (g16 & 1) * 16 + (g16 >> 1) * 8;
 #pragma unroll
-    for (int msl = 0; msl < 2; ++msl)
-#pragma unroll
-      for (int ns = 0; ns < 8; ++ns) {
-        const int row = msl * 16 + r16;
-        const int ch = (ns * 2 + (g16 >> 1)) ^ r16;
-        const v4f v = acc[2 * r + msl][ns];
-        uint2 w;
-        w.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        w.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *reinterpret_cast<uint2*>(X16 + row * 128 + ch * 8 + (g16 & 1) * 4) = w;
-      }
-    wave_sync_lds();
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int idx = it * 64 + lane;
-      const int rl = idx >> 4, cq = idx & 15;
-      const int rt = wm * 64 + 2 * r * 16 + rl;
-      const uint4 v = *reinterpret_cast<const uint4*>(X16 + rl * 128 + ((cq ^ (rl & 15)) * 8));
-      if (rt < cur.rows_valid)
-        *reinterpret_cast<uint4*>(p.y + (size_t)(cur.row0 + rt) * p.N + col0 + cq * 8) = v;
+    for (int ns = 0; ns < 8; ns += 2) {
+      const v4f a = acc[ms][ns], b = acc[ms][ns + 1];
+      const uint32_t a0 = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+      const uint32_t a1 = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+      const uint32_t b0 = (uint32_t)f32_to_bf16(b[0]) | ((uint32_t)f32_to_bf16(b[1]) << 16);
+      const uint32_t b1 = (uint32_t)f32_to_bf16(b[2]) | ((uint32_t)f32_to_bf16(b[3]) << 16);
+      const auto x = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+      const auto z = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+      const uint4 v = {x[0], z[0], x[1], z[1]};
+      if (rt < cur.rows_valid) *reinterpret_cast<uint4*>(yr + ns * 16) = v;
     }
-    wave_sync_lds();
   }
 }
 
@@ -612,16 +594,10 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_kernel(GemmArgs p,
     // barrier of the last block followed the last read); the next tile's
     // first block is in stage S ^ 1 (landed at that barrier) ----
     unsigned char* E = sm + S * STG;
-    if (SWIGLU) {
-      // the epilogue works in registers: stage S is refilled before it
-      if (ld.more) ld.issue(E);
-      epilogue_swiglu<E8M0>(p, cur, acc, smAmax, wm, wn, lane);
-    } else {
-      // staged through stage S, refilled once every wave is done with it
-      epilogue_bf16(p, cur, acc, E, wave, wm, wn, lane);
-      lds_barrier();
-      if (ld.more) ld.issue(E);
-    }
+    // the epilogues work in registers: stage S is refilled before them
+    if (ld.more) ld.issue(E);
+    if (SWIGLU) epilogue_swiglu<E8M0>(p, cur, acc, smAmax, wm, wn, lane);
+    else epilogue_bf16(p, cur, acc, wm, wn, lane);
     S ^= 1;
   }
 }
