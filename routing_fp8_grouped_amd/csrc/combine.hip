@@ -9,11 +9,32 @@
 // order, then the shared row, then the optional residual row (chapter 15
 // lists the residual path among what combine adds), so the result is
 // deterministic.  HBM-bound: (k + 1) BF16 rows read and one written per token.
+// With k known at compile time all of a chunk's row loads are issued before
+// the first is used.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
+__device__ __forceinline__ void add_row(float (&acc)[8], const uint4 v, float wj) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu)), acc[2 * i]);
+    acc[2 * i + 1] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i] >> 16)), acc[2 * i + 1]);
+  }
+}
+__device__ __forceinline__ void add_row(float (&acc)[8], const uint4 v) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
+    acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
+  }
+}
+
+// KC > 0: k == KC, unrolled; KC == 0: any k.
+template <int KC>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ pos,
                                                       const float* __restrict__ w, int k, int d,
@@ -23,45 +44,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   __shared__ int s_pos[16];
   __shared__ float s_w[16];
   const int t = blockIdx.x;
-  if (threadIdx.x < k) {
-    const int p = pos[(size_t)t * k + threadIdx.x];
+  const int kk = KC > 0 ? KC : k;
+  if (threadIdx.x < kk) {
+    const int p = pos[(size_t)t * kk + threadIdx.x];
     const bool ok = p >= 0 && p < rows;   // an unassigned slot contributes nothing
     s_pos[threadIdx.x] = ok ? p : 0;
-    s_w[threadIdx.x] = ok ? w[(size_t)t * k + threadIdx.x] : 0.0f;
+    s_w[threadIdx.x] = ok ? w[(size_t)t * kk + threadIdx.x] : 0.0f;
   }
   __syncthreads();
   const int n8 = d / 8;
-  for (int c = threadIdx.x; c < n8; c += 256) {
+  for (int c = threadIdx.x; c < n8; c += blockDim.x) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)s_pos[j] * d + c * 8);
-      const float wj = s_w[j];
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    if (KC > 0) {
+      uint4 v[KC > 0 ? KC : 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu)), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i] >> 16)), acc[2 * i + 1]);
-      }
-    }
-    if (shared_row0 >= 0) {
-      const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)(shared_row0 + t) * d + c * 8);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      for (int j = 0; j < KC; ++j) v[j] = *reinterpret_cast<const uint4*>(y + (size_t)s_pos[j] * d + c * 8);
+      uint4 vs = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
+      if (shared_row0 >= 0) vs = *reinterpret_cast<const uint4*>(y + (size_t)(shared_row0 + t) * d + c * 8);
+      if (residual) vr = *reinterpret_cast<const uint4*>(residual + (size_t)t * d + c * 8);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
-        acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
-      }
-    }
-    if (residual) {
-      const uint4 v = *reinterpret_cast<const uint4*>(residual + (size_t)t * d + c * 8);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
-        acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
-      }
+      for (int j = 0; j < KC; ++j) add_row(acc, v[j], s_w[j]);
+      if (shared_row0 >= 0) add_row(acc, vs);
+      if (residual) add_row(acc, vr);
+    } else {
+      for (int j = 0; j < k; ++j)
+        add_row(acc, *reinterpret_cast<const uint4*>(y + (size_t)s_pos[j] * d + c * 8), s_w[j]);
+      if (shared_row0 >= 0) add_row(acc, *reinterpret_cast<const uint4*>(y + (size_t)(shared_row0 + t) * d + c * 8));
+      if (residual) add_row(acc, *reinterpret_cast<const uint4*>(residual + (size_t)t * d + c * 8));
     }
     uint4 o;
     o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
@@ -76,8 +87,19 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
                           int d, int shared_row0, const uint16_t* residual, uint16_t* out,
                           hipStream_t stream) {
   const int rows = T * k + (shared_row0 >= 0 ? T : 0);
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, stream, y, pos, w, k, d,
-                     shared_row0 >= 0 ? shared_row0 + T : rows, shared_row0, residual, out);
+  const int rlim = shared_row0 >= 0 ? shared_row0 + T : rows;
+  // threads: the 8-column chunks of a row in equal shares of 128..256 when
+  // there are such shares (224 x 4 for d = 7168), else 256
+  const int n8 = d / 8;
+  int nt = 256;
+  for (int q = (n8 + 255) / 256; n8 / q >= 128; ++q)
+    if (n8 % q == 0) { nt = n8 / q; break; }
+  if (k == 8)
+    hipLaunchKernelGGL(combine_kernel<8>, dim3(T), dim3(nt), 0, stream, y, pos, w, k, d, rlim, shared_row0,
+                       residual, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<0>, dim3(T), dim3(nt), 0, stream, y, pos, w, k, d, rlim, shared_row0,
+                       residual, out);
   return hipGetLastError();
 }
 
