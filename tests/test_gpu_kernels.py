@@ -293,11 +293,19 @@ def test_gemm_parity(counts, d, f, gather):
         f"rows above 5e-3 (within the ambiguity allowance): {n_allow}/{rows}")
 
 
-@pytest.mark.parametrize("with_residual", [False, True])
-def test_combine_parity(with_residual):
-    log(f"combine (residual: {with_residual})")
-    rng = np.random.default_rng(5)
-    T, k, E, d = 300, 8, 64, 512
+# k = 8 takes the unrolled kernel, other k the generic one; a row's 16-byte
+# chunks go to 224 threads x 4 at d = 7168 and 144 x 1 at d = 1152, while
+# d = 512 (64 chunks) runs 256 threads
+@pytest.mark.parametrize("T,k,E,d,with_residual", [
+    (300, 8, 64, 512, False),
+    (300, 8, 64, 512, True),
+    (70, 8, 256, 7168, False),
+    (90, 6, 64, 1152, True),
+    (33, 16, 256, 7168, False),
+])
+def test_combine_parity(T, k, E, d, with_residual):
+    log(f"combine T={T} k={k} d={d} (residual: {with_residual})")
+    rng = np.random.default_rng(5 + T + k)
     idx = random_idx(rng, T, E, k)
     offsets, pos, rt = operm.permute(idx, E)
     rows = T * k + T
