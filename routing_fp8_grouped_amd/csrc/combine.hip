@@ -45,15 +45,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   __shared__ float s_w[16];
   const int t = blockIdx.x;
   const int kk = KC > 0 ? KC : k;
-  if (threadIdx.x < kk) {
-    const int p = pos[(size_t)t * kk + threadIdx.x];
+  const int tid = threadIdx.x;
+  if (tid < kk) {
+    const int p = pos[(size_t)t * kk + tid];
     const bool ok = p >= 0 && p < rows;   // an unassigned slot contributes nothing
-    s_pos[threadIdx.x] = ok ? p : 0;
-    s_w[threadIdx.x] = ok ? w[(size_t)t * kk + threadIdx.x] : 0.0f;
+    s_pos[tid] = ok ? p : 0;
+    s_w[tid] = ok ? w[(size_t)t * kk + tid] : 0.0f;
   }
   __syncthreads();
   const int n8 = d / 8;
-  for (int c = threadIdx.x; c < n8; c += blockDim.x) {
+  for (int c = tid; c < n8; c += (int)blockDim.x) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
