@@ -251,8 +251,39 @@ def gemm_case(rng, counts, d, f, a_rows, gather):
     ([5, 0, 2], 256, 128, False),
 ])
 def test_gemm_parity(counts, d, f, gather):
+    run_gemm_parity(counts, d, f, gather, sum(counts) + d + f)
+
+
+def random_gemm_shape(seed):
+    """Seeded group sizes and widths: seed % 3 picks ragged groups on the tiled
+    kernel, at most 16 rows per group (the weight-streaming kernels), or
+    groups of several tiles (the balanced row split); d = 640 leaves a
+    half-empty last column tile in the second GEMM."""
+    r = np.random.default_rng(1000 + seed)
+    G = int(r.integers(1, 10))
+    d = (128, 640, 384, 256, 512)[seed % 5]   # d = 128: a single K block in the first GEMM
+    f = (384, 128, 256)[(seed // 3) % 3]
+    if seed % 3 == 0:
+        counts = r.integers(0, 300, G)
+    elif seed % 3 == 1:
+        counts = r.integers(0, 17, G)
+    else:
+        counts = np.where(r.random(G) < 0.3, 0, r.integers(200, 600, G))
+    counts = [int(c) for c in counts]
+    if sum(counts) == 0:
+        counts[0] = 1
+    return counts, d, f, bool(r.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(9))
+def test_gemm_parity_random(seed):
+    counts, d, f, gather = random_gemm_shape(seed)
+    run_gemm_parity(counts, d, f, gather, 7 * seed + 1)
+
+
+def run_gemm_parity(counts, d, f, gather, seed):
     log(f"grouped gemm counts={counts} d={d} f={f} gather={gather}")
-    rng = np.random.default_rng(sum(counts) + d + f)
+    rng = np.random.default_rng(seed)
     rows = sum(counts)
     a_rows = max(rows, 40) if gather else rows
     offsets, aq, as_, row_src, experts = gemm_case(rng, counts, d, f, a_rows, gather)
