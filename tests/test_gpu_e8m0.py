@@ -19,7 +19,7 @@ from oracle.gemm import blocked_gemm
 from tests.gpu_util import (DEV, log, to_np, h_noise, h_code_ambiguity, check_h_codes,
                             pow2_scale_choices, rows_within, device_weights, OracleExperts,
                             run_layer, layer_allowance, token_allowance)
-from tests.test_gpu_kernels import bf16_tensor, varied_activations
+from tests.test_gpu_kernels import bf16_tensor, random_gemm_shape, varied_activations
 
 pytestmark = pytest.mark.gpu
 TOL = 5e-3
@@ -128,8 +128,20 @@ def _weights(experts, d, f):
     ([0, 3, 16, 17, 1, 0], 384, 256, True),
 ])
 def test_gemm_e8m0_parity(counts, d, f, gather):
+    run_gemm_e8m0_parity(counts, d, f, gather, sum(counts) * 5 + d + f)
+
+
+# the seeded random shapes of the FP32-scale GEMM test (ragged, <= 16 rows per
+# group, multi-tile groups; d = 128 .. 640, f = 128 .. 384)
+@pytest.mark.parametrize("seed", range(6))
+def test_gemm_e8m0_parity_random(seed):
+    counts, d, f, gather = random_gemm_shape(seed)
+    run_gemm_e8m0_parity(counts, d, f, gather, 11 * seed + 3)
+
+
+def run_gemm_e8m0_parity(counts, d, f, gather, seed):
     log(f"e8m0 grouped gemm counts={counts} d={d} f={f} gather={gather}")
-    rng = np.random.default_rng(sum(counts) * 5 + d + f)
+    rng = np.random.default_rng(seed)
     rows = sum(counts)
     a_rows = max(rows, 40) if gather else rows
     offsets, aq, as_, row_src, experts = pow2_gemm_case(rng, counts, d, f, a_rows, gather)
