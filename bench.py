@@ -201,7 +201,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the MoE layer on a single MI355X "
+        print("bench.py measures one GPU: the MoE layer runs on a single MI355X "
               "(no sharding or collectives); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
