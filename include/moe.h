@@ -305,6 +305,17 @@ moe_status moe_combine_backward(const uint16_t* dout, const uint16_t* y, const i
                                 const float* w, int T, int k, int d, int32_t shared_row0,
                                 uint16_t* dy, float* dw, void* stream);
 
+/* moe_combine_backward_q — moe_combine_backward that also writes the 1x128
+ * power-of-two FP8 copy of every dY row it writes (the Dgrad operand, book
+ * chapter 17: dY enters the backward GEMMs in FP8), bit for bit what
+ * fp8_quant_1x128_pow2 makes of dy, without reading dy back:
+ *   dyq [rows, d] E4M3 codes, dys [rows, d/128] FP32 scales (rows written by
+ *   this call only; other rows untouched).  Same arguments and errors
+ *   otherwise. */
+moe_status moe_combine_backward_q(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
+                                  const float* w, int T, int k, int d, int32_t shared_row0,
+                                  uint16_t* dy, float* dw, uint8_t* dyq, float* dys, void* stream);
+
 /* moe_wgrad_columns — Kp of the K-major layout for total_rows rows in n_groups
  * groups: 128 * (total_rows / 128 + n_groups), an upper bound of
  * 128 pb[n_groups] that depends only on host-known sizes (0 on bad input). */

@@ -240,16 +240,25 @@ def moe_transpose_fp8_blocks(w, ws, wt, wts, stream=None):
         _ptr(w), _ptr(ws), G, N, K, _ptr(wt), _ptr(wts), _stream(stream)))
 
 
-def moe_combine_backward(dout, y, pos, w, shared_row0, dy, dw, stream=None):
-    """dy [rows, d] BF16 and dw [T, k] FP32 from dout [T, d] and the forward's y."""
+def moe_combine_backward(dout, y, pos, w, shared_row0, dy, dw, stream=None, dyq=None, dys=None):
+    """dy [rows, d] BF16 and dw [T, k] FP32 from dout [T, d] and the forward's y;
+    with dyq [rows, d] uint8 and dys [rows, d/128] FP32 also the 1x128
+    power-of-two FP8 copy of the dY rows (moe_combine_backward_q)."""
     for t, dt, n in ((dout, torch.bfloat16, "dout"), (y, torch.bfloat16, "y"), (pos, torch.int32, "pos"),
                      (w, torch.float32, "w"), (dy, torch.bfloat16, "dy"), (dw, torch.float32, "dw")):
         _dev(t, dt, n)
     T, k = pos.shape
     lib = _lib.load()
-    _lib.check("moe_combine_backward", lib.moe_combine_backward(
+    if dyq is None and dys is None:
+        _lib.check("moe_combine_backward", lib.moe_combine_backward(
+            _ptr(dout), _ptr(y), _ptr(pos), _ptr(w), T, k, dout.shape[1], shared_row0, _ptr(dy),
+            _ptr(dw), _stream(stream)))
+        return
+    _dev(dyq, torch.uint8, "dyq")
+    _dev(dys, torch.float32, "dys")
+    _lib.check("moe_combine_backward_q", lib.moe_combine_backward_q(
         _ptr(dout), _ptr(y), _ptr(pos), _ptr(w), T, k, dout.shape[1], shared_row0, _ptr(dy),
-        _ptr(dw), _stream(stream)))
+        _ptr(dw), _ptr(dyq), _ptr(dys), _stream(stream)))
 
 
 def moe_wgrad_columns(total_rows, n_groups):
@@ -452,8 +461,8 @@ class MoELayer:
         mark = mark or (lambda name: None)
         T, k, d, f, E = self.T, self.k, self.d, self.f, self.E
         rows, G = T * k + T, E + 1
-        moe_combine_backward(dout, self.y, self.pos, self.w, T * k, self.dy, self.dw, stream)
-        fp8_quant_1x128_pow2(self.dy, self.dyq, self.dys, stream)
+        moe_combine_backward(dout, self.y, self.pos, self.w, T * k, self.dy, self.dw, stream,
+                             dyq=self.dyq, dys=self.dys)
         mark("combine_bwd")
         grouped_gemm_fp8_down(self.dyq, self.dys, self.offsets, weights_t.w2q, weights_t.w2s, self.dh, stream)
         mark("dgrad_w2")

@@ -54,6 +54,7 @@ SIGNATURES = {
     "grouped_gemm_fp8_down_e8m0": (I, [P, P, P, I, I, I, I, P, P, P, P]),
     "moe_transpose_fp8_blocks": (I, [P, P, I, I, I, P, P, P]),
     "moe_combine_backward": (I, [P, P, P, P, I, I, I, ctypes.c_int32, P, P, P]),
+    "moe_combine_backward_q": (I, [P, P, P, P, I, I, I, ctypes.c_int32, P, P, P, P, P]),
     "moe_wgrad_columns": (I, [I, I]),
     "moe_regroup_128x1": (I, [P, P, P, P, P, I, I, I, P, P, P]),
     "moe_swiglu_backward": (I, [P, P, P, P, I, I, I, P, P, P, P, P, P, P]),

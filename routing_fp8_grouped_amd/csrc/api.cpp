@@ -428,9 +428,32 @@ moe_status moe_combine_backward(const uint16_t* dout, const uint16_t* y, const i
   REQUIRE_PTR4(w);
   REQUIRE_PTR(dy);
   REQUIRE_PTR4(dw);
-  return hip_status(moe::launch_combine_backward(dout, y, pos, w, T, k, d, shared_row0, dy, dw,
-                                                 static_cast<hipStream_t>(stream)),
+  return hip_status(moe::launch_combine_backward(dout, y, pos, w, T, k, d, shared_row0, dy, dw, nullptr,
+                                                 nullptr, static_cast<hipStream_t>(stream)),
                     "moe_combine_backward launch");
+}
+
+moe_status moe_combine_backward_q(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
+                                  const float* w, int T, int k, int d, int32_t shared_row0, uint16_t* dy,
+                                  float* dw, uint8_t* dyq, float* dys, void* stream) {
+  clear_error();
+  REQUIRE(T >= 0, "T=%d is negative", T);
+  REQUIRE(k >= 1 && k <= 16, "k=%d must be in [1, 16]", k);
+  REQUIRE(d >= 128 && d % 128 == 0, "d=%d must be a positive multiple of 128", d);
+  REQUIRE(shared_row0 >= -1, "shared_row0=%d must be >= -1", shared_row0);
+  if (T == 0) return MOE_OK;
+  REQUIRE(T <= INT32_MAX / (k + 1), "T*(k+1) overflows int32");
+  REQUIRE_PTR(dout);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR4(pos);
+  REQUIRE_PTR4(w);
+  REQUIRE_PTR(dy);
+  REQUIRE_PTR4(dw);
+  REQUIRE_PTR(dyq);
+  REQUIRE_PTR4(dys);
+  return hip_status(moe::launch_combine_backward(dout, y, pos, w, T, k, d, shared_row0, dy, dw, dyq, dys,
+                                                 static_cast<hipStream_t>(stream)),
+                    "moe_combine_backward_q launch");
 }
 
 int moe_wgrad_columns(int total_rows, int n_groups) {

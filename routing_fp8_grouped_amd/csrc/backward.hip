@@ -96,10 +96,35 @@ __global__ __launch_bounds__(256) void transpose_blocks_kernel(const uint8_t* __
 // ---- combine backward: one workgroup per token ----
 // dy[pos[t][j]] = BF16(w[t][j] * dout[t]); dy[shared_row0 + t] = dout[t];
 // dw[t][j] = sum_c dout[t][c] * y[pos[t][j]][c] in FP32.
+// Q: also the 1x128 power-of-two FP8 copy of every dY row written (dyq, dys),
+// the same arithmetic as fp8_quant_1x128_pow2 on dy: the 16 threads of a 1x128
+// tile hold 8 consecutive elements each (256 threads cover 16 whole tiles).
+__device__ __forceinline__ void quant_chunk_pow2(const uint32_t (&o)[4], uint8_t* __restrict__ q, float* sq,
+                                                 bool first) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(static_cast<uint16_t>(o[i] & 0xFFFFu));
+    v[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(o[i] >> 16));
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o2 = 8; o2 > 0; o2 >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o2));
+  const float sc = tile_scale<true>(amax);
+  uint2 out;
+  out.x = f32x4_to_e4m3(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+  out.y = f32x4_to_e4m3(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
+  *reinterpret_cast<uint2*>(q) = out;
+  if (first) *sq = sc;
+}
+
+template <bool Q>
 __global__ __launch_bounds__(256) void combine_backward_kernel(
     const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y, const int32_t* __restrict__ pos,
     const float* __restrict__ w, int k, int d, int shared_row0, uint16_t* __restrict__ dy,
-    float* __restrict__ dw) {
+    float* __restrict__ dw, uint8_t* __restrict__ dyq, float* __restrict__ dys) {
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint16_t* go = dout + (size_t)t * d;
@@ -122,6 +147,8 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
         o[i] = (uint32_t)f32_to_bf16(wt * a0) | ((uint32_t)f32_to_bf16(wt * a1) << 16);
       }
       *reinterpret_cast<uint4*>(dy + (size_t)row * d + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+      if (Q) quant_chunk_pow2(o, dyq + (size_t)row * d + c * 8, dys + (size_t)row * (d / 128) + (c >> 4),
+                              (c & 15) == 0);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
@@ -131,9 +158,15 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
     __syncthreads();
   }
   if (shared_row0 >= 0)
-    for (int c = tid; c < n8; c += 256)
-      *reinterpret_cast<uint4*>(dy + (size_t)(shared_row0 + t) * d + c * 8) =
-          *reinterpret_cast<const uint4*>(go + c * 8);
+    for (int c = tid; c < n8; c += 256) {
+      const uint4 v = *reinterpret_cast<const uint4*>(go + c * 8);
+      const size_t row = (size_t)(shared_row0 + t);
+      *reinterpret_cast<uint4*>(dy + row * d + c * 8) = v;
+      if (Q) {
+        const uint32_t o[4] = {v.x, v.y, v.z, v.w};
+        quant_chunk_pow2(o, dyq + row * d + c * 8, dys + row * (d / 128) + (c >> 4), (c & 15) == 0);
+      }
+    }
 }
 
 // ---- 128x1 regrouping into the K-major layout ----
@@ -408,9 +441,13 @@ hipError_t launch_transpose_blocks(const uint8_t* w, const float* ws, int G, int
 
 hipError_t launch_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
                                    const float* w, int T, int k, int d, int shared_row0, uint16_t* dy,
-                                   float* dw, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_backward_kernel, dim3(T), dim3(256), 0, stream, dout, y, pos, w, k, d,
-                     shared_row0, dy, dw);
+                                   float* dw, uint8_t* dyq, float* dys, hipStream_t stream) {
+  if (dyq)
+    hipLaunchKernelGGL(combine_backward_kernel<true>, dim3(T), dim3(256), 0, stream, dout, y, pos, w, k, d,
+                       shared_row0, dy, dw, dyq, dys);
+  else
+    hipLaunchKernelGGL(combine_backward_kernel<false>, dim3(T), dim3(256), 0, stream, dout, y, pos, w, k, d,
+                       shared_row0, dy, dw, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ hipError_t launch_transpose_blocks(const uint8_t* w, const float* ws, int G, int
                                    float* wts, hipStream_t stream);
 hipError_t launch_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
                                    const float* w, int T, int k, int d, int shared_row0, uint16_t* dy,
-                                   float* dw, hipStream_t stream);
+                                   float* dw, uint8_t* dyq, float* dys, hipStream_t stream);
 int wgrad_blocks_bound(int total_rows, int n_groups);
 hipError_t launch_regroup_128x1(const uint8_t* xq, const float* xs, const uint16_t* xb,
                                 const int32_t* row_src, const int32_t* offsets, int n_groups,

@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(lib):
                              "fp8_quant_1x128_pow2", "fp8_quant_128x128_pow2",
                              "grouped_gemm_fp8_up_e8m0", "grouped_gemm_fp8_down_e8m0",
                              "grouped_gemm_fp8_up_train", "moe_transpose_fp8_blocks",
-                             "moe_combine_backward", "moe_wgrad_columns", "moe_regroup_128x1",
+                             "moe_combine_backward", "moe_combine_backward_q",
+                             "moe_wgrad_columns", "moe_regroup_128x1",
                              "moe_swiglu_backward", "grouped_gemm_fp8_wgrad",
                              "moe_status_string", "moe_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -213,6 +214,12 @@ def test_backward_validation(lib):
     assert lib.moe_combine_backward(A, A, A, A, 10, 0, 256, 80, A, A, None) == 1
     assert lib.moe_combine_backward(A, A, A, MIS4, 10, 8, 256, 80, A, A, None) == 1
     assert lib.moe_combine_backward(None, None, None, None, 0, 8, 256, 0, None, None, None) == 0
+    # the quantising form: its two extra outputs are checked like the others
+    assert lib.moe_combine_backward_q(A, A, A, A, 10, 8, 256, 80, A, A, None, A, None) == 1 \
+        and "dyq is NULL" in last(lib)
+    assert lib.moe_combine_backward_q(A, A, A, A, 10, 8, 256, 80, A, A, A, MIS4, None) == 1
+    assert lib.moe_combine_backward_q(A, A, A, A, 10, 8, 100, 80, A, A, A, A, None) == 1 and "d=100" in last(lib)
+    assert lib.moe_combine_backward_q(None, None, None, None, 0, 8, 256, 0, None, None, None, None, None) == 0
     # exactly one source for the regrouping
     assert lib.moe_regroup_128x1(A, A, A, None, A, 3, 100, 256, A, A, None) == 1 and "exactly one" in last(lib)
     assert lib.moe_regroup_128x1(None, None, A, A, A, 3, 100, 256, A, A, None) == 1 and "row_src" in last(lib)

@@ -94,6 +94,39 @@ def test_combine_backward():
     assert np.all(np.abs(to_np(dw) - rdw) <= bound + 1e-30)
 
 
+@pytest.mark.parametrize("T,k,E,d", [(37, 4, 16, 384), (64, 8, 256, 7168)])
+def test_combine_backward_quantising(T, k, E, d):
+    """moe_combine_backward_q: the same dY and gate gradients, and the 1x128
+    power-of-two copy of dY bit for bit what fp8_quant_1x128_pow2 makes of it
+    and what the oracle's power-of-two rule makes of its dY."""
+    log(f"combine backward with dY quantisation T={T} k={k} d={d}")
+    rng = np.random.default_rng(20 + T)
+    idx = np.stack([np.sort(rng.choice(E, k, replace=False)) for _ in range(T)])
+    _, pos, _ = operm.permute(idx, E)
+    rows = T * k + T
+    y = bf16_tensor(rng.standard_normal((rows, d)))
+    dout = bf16_tensor(rng.standard_normal((T, d)) * np.exp(rng.normal(0, 2, (T, 1))))
+    w = rng.uniform(0.05, 1.0, (T, k)).astype(np.float32)
+    dy = torch.empty(rows, d, dtype=torch.bfloat16, device=DEV)
+    dw = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    dyq = torch.empty(rows, d, dtype=torch.uint8, device=DEV)
+    dys = torch.empty(rows, d // 128, dtype=torch.float32, device=DEV)
+    dw0 = torch.empty_like(dw)
+    dy0 = torch.empty_like(dy)
+    moe.moe_combine_backward(dout.to(DEV), y.to(DEV), D(pos), D(w), T * k, dy0, dw0)
+    moe.moe_combine_backward(dout.to(DEV), y.to(DEV), D(pos), D(w), T * k, dy, dw, dyq=dyq, dys=dys)
+    q2 = torch.empty_like(dyq)
+    s2 = torch.empty_like(dys)
+    moe.fp8_quant_1x128_pow2(dy, q2, s2)
+    torch.cuda.synchronize()
+    rdy, _ = ob.combine_backward(dout.float().numpy(), y.float().numpy(), w, pos, T, k)
+    assert np.array_equal(to_np(dy), rdy)
+    assert torch.equal(dy.view(torch.int16), dy0.view(torch.int16)) and torch.equal(dw, dw0)
+    assert torch.equal(dyq, q2) and torch.equal(dys, s2)
+    rq, rs = oq.quant_1x128(rdy, "pow2")
+    assert np.array_equal(to_np(dyq), rq) and np.array_equal(to_np(dys), rs)
+
+
 def _routing(rng, T, k, E, empty=()):
     allowed = [e for e in range(E) if e not in empty]
     idx = np.stack([np.sort(rng.choice(allowed, k, replace=False)) for _ in range(T)])
