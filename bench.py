@@ -89,11 +89,15 @@ def cpu_baseline(cfg, n_tokens):
     and the combine."""
     import concurrent.futures as cf
     from oracle import layer as olayer, route as oroute
+    # host cores this process may run on, and the threads numpy's BLAS uses
+    # for the oracle's products (the rest of the oracle is one Python thread)
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        cores = os.cpu_count() or 1
+        blas = affinity
+    cores = min(affinity, blas)
     x = inputs.activations(cfg, T=n_tokens).float().numpy()
     wg = inputs.router_weights(cfg).float().numpy()
     b = inputs.selection_bias(cfg).numpy()
@@ -112,9 +116,12 @@ def cpu_baseline(cfg, n_tokens):
     olayer.moe_layer_tokens(x, wg, b, lambda e: q[e], cfg.G, cfg.M, cfg.k, cfg.route_scale)
     dt = time.perf_counter() - t0
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "affinity_cores": affinity, "blas_threads": int(blas),
             "sample": f"first {n_tokens} token(s) of the {cfg.name} workload, whole layer "
                       f"({len(need)} experts incl. shared), {dt:.1f} s; expert weights "
-                      "quantised by the oracle beforehand (untimed, as on the GPU)"}
+                      "quantised by the oracle beforehand (untimed, as on the GPU); cores = "
+                      "min(sched_getaffinity cores, BLAS threads): the oracle's products run "
+                      "on the BLAS threads, its loops on one Python thread"}
 
 
 def timed_steps(layer, x, wg, b, W, steps):

@@ -80,7 +80,10 @@ typedef struct {
  * blocks summed in FP64); selection score z = s + b; group score = sum of the
  * k/M largest z in the group; the M best groups are kept (ties to the lower
  * group index); the k largest z among their experts are selected (ties to the
- * lower expert index).  Selection and gates are evaluated in FP64. */
+ * lower expert index).  The selection ranks FP32 biased scores: the logit
+ * rounded to FP32, an FP32 sigmoid (exp and the hardware reciprocal, a few
+ * ulp from exact), plus the bias; ranks move only within 1e-6 near ties.
+ * The gates are evaluated in FP64 and rounded to FP32. */
 moe_status moe_route(const uint16_t* x, const uint16_t* wg, const float* bias,
                      int T, int d, moe_route_params p,
                      int32_t* idx, float* w, void* stream);
@@ -300,7 +303,10 @@ moe_status moe_transpose_fp8_blocks(const uint8_t* w, const float* ws, int n_mat
  *   dw[t][j]          = sum_c dout[t][c] * y[pos[t][j]][c]   (FP32 sum)
  *   dy[shared_row0+t] = dout[t]   (when shared_row0 >= 0)
  *   dout [T, d] BF16; y [rows, d] BF16 (the forward's expert outputs);
- *   pos, w [T, k]; dy [rows, d] BF16 out; dw [T, k] FP32 out. */
+ *   pos, w [T, k]; dy [rows, d] BF16 out; dw [T, k] FP32 out.
+ * rows = shared_row0 + T (T*k without a shared expert), as for moe_combine; a
+ * slot whose pos lies outside [0, rows) (an unassigned slot) gets dw = 0 and
+ * writes no dY row. */
 moe_status moe_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
                                 const float* w, int T, int k, int d, int32_t shared_row0,
                                 uint16_t* dy, float* dw, void* stream);

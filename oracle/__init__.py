@@ -30,7 +30,13 @@ fp8.e4m3_*      the format table on "DeepSeek-V3: the recipe, and the interconne
 fp8.bf16_*      torch's bfloat16 conversion on random and tie inputs.
 quant.*         exact round trip of values already on the E4M3 grid; the quiet-value
                 error statistic printed on the same page (block 128: 0.026348) as a
-                loose statistical pin; the 4096x7168 byte count (30.28 MB).
+                loose statistical pin; the 4096x7168 byte count (30.28 MB); the FP32
+                rule scale = fl32(amax/448), code = E4M3(fl32(x/scale)) against exact
+                rational arithmetic on a non-power-of-two scale, on values where a
+                reciprocal multiply gives another code, and on values where
+                fl32(x/scale) lands on an E4M3 midpoint that x/scale does not
+                (tests/test_oracle_quant_rule.py); the power-of-two rule against hand
+                values and an enumeration of exponents.
 route.route     the two worked examples of the book's chapter 7 ("A toy mixture")
                 and chapter 8 ("A selection-versus-weighting example"); brute-force
                 enumeration of group subsets and expert subsets on tiny inputs;
@@ -43,7 +49,9 @@ layer.*         SwiGLU closed form; k = E dense special case; route_scale = 0 gi
                 the shared expert alone; sampled-token evaluation equals the
                 full-batch evaluation.
 
-No function here is "parity unpinned".
+Every function above has at least one pin that does not restate its own
+formula.  What no pin reaches: the whole-layer output at the V3 shape (no page
+prints one); it rests on the pins of its parts and on the k = E dense case.
 """
 
 from . import fp8, quant, route, permute, gemm, layer  # noqa: F401

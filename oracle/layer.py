@@ -8,14 +8,14 @@ the top K_r get a nonzero gate.  Each expert is a SwiGLU FFN with input/output
 width d and two intermediate branches of width f (chapter 7 "What one expert
 computes"; the equation is missing from the extracted text, so the reading is
 the standard SwiGLU  FFN(x) = W2 (SiLU(W1 x) * (W3 x)), SiLU(z) = z / (1 + e^-z),
-no biases).  All principal GEMMs take FP8 inputs (summary page section 6, "All
-three GEMMs of each linear layer run in FP8"), so the SwiGLU output is
-quantised in 1x128 tiles before the down projection, as the SwiGLU inputs are
-cached in FP8 (chapter 17 "SwiGLU recomputation").  Expert outputs and the
-combine stay BF16 (summary page section 6 "Storage and communication"; chapter
-17 "FP8 dispatch, BF16 combine").  The combine adds the gated routed outputs and
-the shared expert's output; the residual stays outside the layer (chapter 7:
-"the residual u remains, and the shared expert is added separately").
+no biases).  The summary page's section 6 keeps every principal GEMM of a
+linear layer in FP8, so the SwiGLU output is quantised in 1x128 tiles before
+the down projection, as the SwiGLU inputs are cached in FP8 (chapter 17
+"SwiGLU recomputation").  Expert outputs and the combine stay BF16 (summary
+page section 6 "Storage and communication"; chapter 17 "FP8 dispatch, BF16
+combine").  The combine adds the gated routed outputs and the shared expert's
+output; the residual connection is kept apart from the expert sum and added by
+the caller (chapter 7, "Selecting and combining experts").
 
 Rounding points emulated (readings): the GEMM outputs G and U are rounded to
 FP32; h = fl32(SiLU(g) * u); each expert output is fl32 then BF16; the combine

@@ -123,7 +123,7 @@ __device__ __forceinline__ void quant_chunk_pow2(const uint32_t (&o)[4], uint8_t
 template <bool Q>
 __global__ __launch_bounds__(256) void combine_backward_kernel(
     const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y, const int32_t* __restrict__ pos,
-    const float* __restrict__ w, int k, int d, int shared_row0, uint16_t* __restrict__ dy,
+    const float* __restrict__ w, int k, int d, int rows, int shared_row0, uint16_t* __restrict__ dy,
     float* __restrict__ dw, uint8_t* __restrict__ dyq, float* __restrict__ dys) {
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -132,6 +132,12 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
   for (int j = 0; j < k; ++j) {
     const int row = pos[t * k + j];
     const float wt = w[t * k + j];
+    // a slot outside the rows (an unassigned one, pos < 0) has no expert
+    // output: its gate gradient is 0 and no dY row is written (uniform branch)
+    if (row < 0 || row >= rows) {
+      if (tid == 0) dw[t * k + j] = 0.0f;
+      continue;
+    }
     float part = 0.0f;
     for (int c = tid; c < n8; c += 256) {
       const uint4 a = *reinterpret_cast<const uint4*>(go + c * 8);
@@ -442,12 +448,14 @@ hipError_t launch_transpose_blocks(const uint8_t* w, const float* ws, int G, int
 hipError_t launch_combine_backward(const uint16_t* dout, const uint16_t* y, const int32_t* pos,
                                    const float* w, int T, int k, int d, int shared_row0, uint16_t* dy,
                                    float* dw, uint8_t* dyq, float* dys, hipStream_t stream) {
+  // rows of y / dy (the same bound as the forward combine's)
+  const int rlim = shared_row0 >= 0 ? shared_row0 + T : T * k;
   if (dyq)
     hipLaunchKernelGGL(combine_backward_kernel<true>, dim3(T), dim3(256), 0, stream, dout, y, pos, w, k, d,
-                       shared_row0, dy, dw, dyq, dys);
+                       rlim, shared_row0, dy, dw, dyq, dys);
   else
     hipLaunchKernelGGL(combine_backward_kernel<false>, dim3(T), dim3(256), 0, stream, dout, y, pos, w, k, d,
-                       shared_row0, dy, dw, nullptr, nullptr);
+                       rlim, shared_row0, dy, dw, nullptr, nullptr);
   return hipGetLastError();
 }
 

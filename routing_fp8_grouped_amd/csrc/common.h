@@ -60,6 +60,30 @@ __device__ __forceinline__ float scale_from_amax_pow2(float amax) {
   return (b & 0x007FFFFFu) ? __uint_as_float((b & 0x7F800000u) + 0x00800000u) : __uint_as_float(b);
 }
 
+// h = SiLU(g) * u with SiLU(g) = g / (1 + e^-g) in FP32: exp within an ulp,
+// then correctly rounded addition, division and product, so h is within
+// 2.5 ulp of the exactly rounded value (no hardware reciprocal estimate).
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+// x / s for many x with one s, correctly rounded: r = 1/s is computed once by
+// IEEE division (correctly rounded).  Per x, q0 = x r is within 1.5 ulp of x/s;
+// one correction q1 = q0 + r (x - s q0) brings it within an ulp, so the next
+// remainder x - s q1 is exact by FMA and q1 + r (x - s q1) rounds to the
+// correctly rounded quotient (Markstein's theorem on division with a correctly
+// rounded reciprocal; no overflow or underflow here).  An exact zero keeps its
+// sign.
+struct Divider {
+  float s, r;
+  __device__ __forceinline__ explicit Divider(float s_) : s(s_), r(1.0f / s_) {}
+  __device__ __forceinline__ float operator()(float x) const {
+    const float q0 = x * r;
+    const float q1 = fmaf(fmaf(-s, q0, x), r, q0);
+    return x == 0.0f ? q0 : fmaf(fmaf(-s, q1, x), r, q1);
+  }
+};
+
 template <bool POW2>
 __device__ __forceinline__ float tile_scale(float amax) {
   return POW2 ? scale_from_amax_pow2(amax) : scale_from_amax(amax);

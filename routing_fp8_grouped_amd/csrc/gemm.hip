@@ -240,25 +240,6 @@ __device__ __forceinline__ v8i frag(const unsigned char* T, int r, int g16) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// SiLU(g) * u in FP32: exp(-g) to within an ulp, the quotient by the hardware
-// reciprocal (1 ulp); a few ulp from the exactly rounded value.
-__device__ __forceinline__ float swiglu(float g, float u) {
-  return g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * u;
-}
-
-// x / s for many x with one s: the reciprocal r (hardware estimate refined by
-// one Newton step), then per x the product, its exact remainder by FMA and one
-// correction (Markstein's sequence): the correctly rounded quotient but in rare
-// cases next to a rounding boundary, where it is one ulp off.
-__device__ __forceinline__ float recip(float s) {
-  const float r = __builtin_amdgcn_rcpf(s);
-  return fmaf(fmaf(-s, r, 1.0f), r, r);
-}
-__device__ __forceinline__ float div_by(float x, float s, float r) {
-  const float q = x * r;
-  return fmaf(fmaf(-s, q, x), r, q);
-}
-
 // ---- epilogues ----
 // With the weight fragment as the MFMA's first operand, lane (g16, r16) holds
 // in acc[ms][ns] row ms*16 + r16 of the wave's 64 rows and the 4 consecutive
@@ -290,14 +271,14 @@ __device__ __forceinline__ void quantise_rows(const v4f (&acc)[4][8], int j0, fl
   for (int ms = 0; ms < 4; ++ms) {
     const int rt = wm * 64 + ms * 16 + r16;
     const float sc = tile_scale<POW2>(fmaxf(smAmax[0][rt], smAmax[1][rt]));
-    const float rs = recip(sc);
+    const Divider div(sc);
     const bool ok = rt < cur.rows_valid;
     if (wn == 0 && g16 == 0 && ok) sout[(size_t)(cur.row0 + rt) * sld] = sc;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const v4f v = acc[ms][j0 + j];
-      const uint32_t q = f32x4_to_e4m3(div_by(v[0], sc, rs), div_by(v[1], sc, rs), div_by(v[2], sc, rs),
-                                       div_by(v[3], sc, rs));
+      // correctly rounded FP32 quotients, as in the activation quantiser
+      const uint32_t q = f32x4_to_e4m3(div(v[0]), div(v[1]), div(v[2]), div(v[3]));
       if (ok) *reinterpret_cast<uint32_t*>(out + (size_t)(cur.row0 + rt) * ld + j * 16) = q;
     }
   }
@@ -324,7 +305,7 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& p, const Tile& c
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[ms][j][e] = swiglu(acc[ms][j][e], acc[ms][4 + j][e]);
+      for (int e = 0; e < 4; ++e) acc[ms][j][e] = swiglu_f32(acc[ms][j][e], acc[ms][4 + j][e]);
   quantise_rows<POW2>(acc, 0, smAmax, wm, wn, g16, r16, cur, p.h + col, (size_t)p.f, p.hs + cur.n, nhs);
 }
 

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float gv = acc0[i], uv = acc1[i];
-        hv[i] = gv * __builtin_amdgcn_rcpf(1.0f + expf(-gv)) * uv;
+        hv[i] = swiglu_f32(gv, uv);
         float a = fabsf(hv[i]);
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
@@ -215,10 +215,7 @@ __global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
         for (int w = 1; w < SM_THREADS / 64; ++w) a = fmaxf(a, sAmax[w][r]);
         const float sc = tile_scale<POW2>(a);
         if (r < rows_valid) {
-          const float rs = __builtin_amdgcn_rcpf(sc);
-          const float r1 = fmaf(fmaf(-sc, rs, 1.0f), rs, rs);   // reciprocal, one Newton step
-          const float q0 = hv[i] * r1;
-          const float qv = fmaf(fmaf(-sc, q0, hv[i]), r1, q0);  // h / sc, one correction
+          const float qv = Divider(sc)(hv[i]);   // correctly rounded FP32 quotient
           p.h[(size_t)(row0 + r) * p.f + n * 128 + wave * 16 + r16] =
               (uint8_t)(f32x2_to_e4m3(qv, 0.0f) & 0xFFu);
           if (wave == 0 && r16 == 0) p.hs[(size_t)(row0 + r) * nhs + n] = sc;

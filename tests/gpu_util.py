@@ -102,19 +102,20 @@ def run_layer(cfg, x, wg, b, W, dispatch=False, scales="fp32"):
 # ---- codes of h with two valid values ------------------------------------------
 #
 # The GPU computes each 128-wide K block's partial sum with one E4M3 MFMA, which
-# sums its 128 products with an unbiased error of RMS 1.87e-6 and at most
-# 1.39e-5 of sum|a*b| (measured on gfx950 over 1M dot products of random
-# quantised tiles).  G and U, and
+# sums its 128 products with an unbiased error of RMS 1.87e-6 of sum|a*b|, and
+# at most 1.75e-5 of it over 3 x 1M dot products of E4M3 codes of Gaussian
+# tiles (measured on gfx950 by tests/test_gpu_mfma_noise.py; the tail is heavy:
+# 9.6 RMS).  MFMA_BLOCK_MAX takes 1.4 times that maximum.  G and U, and
 # so h = SiLU(G) * U, therefore differ from the oracle's exact blocked sums by a
 # small, bounded amount, and an element of h that lies that close to an E4M3
 # rounding midpoint has two correct codes.  These helpers flag such elements
 # from oracle quantities alone and bound what a one-step code change can do to
 # the expert output, the way near-tie tokens are handled for routing.
 
-from oracle import fp8 as ofp8, quant as oquant
+from oracle import fp8 as ofp8, quant as oquant, gemm as ogemm
 
 MFMA_BLOCK_RMS = 1.87e-6   # RMS of (block sum - exact) / sum|a*b|
-MFMA_BLOCK_MAX = 1.39e-5   # largest observed |block sum - exact| / sum|a*b|
+MFMA_BLOCK_MAX = 2.5e-5    # bound on |block sum - exact| / sum|a*b| (measured max 1.75e-5)
 
 
 def block_abs_sums(aq_rows, as_rows, wq, ws):
@@ -135,14 +136,16 @@ def block_abs_sums(aq_rows, as_rows, wq, ws):
 
 
 # Over 56 K blocks (K = 7168) on E4M3 codes of Gaussian data, measured on
-# gfx950 over 131,072 outputs: |error| has RMS 1.07 sigma (sigma = the RMS above
-# times the root-sum-square of the blocks' s*sum|a*b|), maximum 6.58 sigma and
-# 1.92 times the single-block bound; chaining the accumulator through the
-# block-scaled instruction gives the same errors as promoting each partial in
-# FP32.  The band takes 8 sigma and 3 times the single-block bound, for a
-# margin over the tails of the ~10^6 outputs of a test.
+# gfx950 over 131,072 outputs (tests/test_gpu_mfma_noise.py): |error| has RMS
+# 1.07 sigma (sigma = the RMS above times the root-sum-square of the blocks'
+# s*sum|a*b|) and a maximum of 6.6 sigma, and stays within 1.1 times the
+# single-block bound MFMA_BLOCK_MAX * max over blocks of s*sum|a*b|; chaining
+# the accumulator through the block-scaled instruction gives the same errors
+# as promoting each partial in FP32.  The band takes 8 sigma and twice the
+# single-block bound, for a margin over the tails of the ~10^6 outputs of a
+# test.
 NOISE_SIGMAS = 8.0
-NOISE_BLOCKS = 3.0
+NOISE_BLOCKS = 2.0
 
 
 def gemm_noise(aq_rows, as_rows, wq, ws, acc):
@@ -195,9 +198,15 @@ def h_noise(aq_rows, as_rows, w13q, w13s, g, u, h):
     eg, eu = e[:, :f], e[:, f:]
     sig = 1.0 / (1.0 + np.exp(-g))
     dsilu = sig * (1.0 + g * (1.0 - sig))
-    # FP32 SwiGLU: the kernel's SiLU (exp within an ulp, hardware reciprocal)
-    # and the product with u sit a few ulp from the exactly rounded value
-    return np.abs(u) * np.abs(dsilu) * eg + np.abs(g * sig) * eu + 2.0 ** -20 * np.abs(h)
+    return np.abs(u) * np.abs(dsilu) * eg + np.abs(g * sig) * eu + SWIGLU_REL * np.abs(h)
+
+
+# The kernels' SwiGLU is g / (1 + exp(-g)) * u in FP32: exp within one ulp, then
+# a correctly rounded sum, quotient and product, so h is within 2.5 ulp (at
+# most 2.5 * 2^-23 relative) of fl32(SiLU(g) * u) for the same g and u.  The
+# h/scale division of the requantisation is correctly rounded, as in the
+# oracle.
+SWIGLU_REL = 2.0 ** -21
 
 
 def pow2_scale_choices(h, eh):
@@ -296,7 +305,55 @@ def rows_within(got, ref, allow, tol):
     nref = np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
     nall = np.linalg.norm(allow, axis=-1)
     ok = err <= tol * nref + nall
+    rows_within.allow_rel = nall / nref     # for reports
     return ok, err / nref, int(np.sum(err > tol * nref))
+
+
+def chain_report(err, allow_rel, tol):
+    """One line on the independent chain (GPU layer against the oracle's own
+    chain): rows above tol form a counted category, like near-tie tokens,
+    each explained by SwiGLU outputs within the MFMA's noise of an E4M3
+    rounding midpoint; the size of that allowance is printed."""
+    over = err > tol
+    return (f"independent chain: rel-L2 max {err.max():.2e} median {np.median(err):.2e}; "
+            f"rows above {tol:.0e}: {int(over.sum())} of {err.size} (max {err.max():.2e}); "
+            f"allowance ||allow||/||ref|| median {np.median(allow_rel):.2e} max {allow_rel.max():.2e}"
+            + (f", on those rows max {allow_rel[over].max():.2e}" if over.any() else ""))
+
+
+# ---- stage-fed check: the GPU's own H through the oracle's last stages ----------
+
+def oracle_down_rows(hq, hs, experts_of_rows, experts):
+    """The oracle's down projection of H rows given as codes and scales
+    (e.g. the GPU's own): y = BF16(fl32(blocked GEMM with W2 of each row's
+    expert)), float32 [rows, d]."""
+    hq = np.asarray(hq); hs = np.asarray(hs, np.float32)
+    ids = np.asarray(experts_of_rows)
+    out = None
+    for e in np.unique(ids):
+        sel = np.nonzero(ids == e)[0]
+        _, _, w2q, w2s = experts(int(e))
+        y = ofp8.bf16_round(ofp8.f32(ogemm.blocked_gemm(hq[sel], hs[sel], w2q, w2s)))
+        if out is None:
+            out = np.zeros((ids.size, y.shape[1]), np.float32)
+        out[sel] = y
+    return out
+
+
+def stage_fed_tokens(L, tokens, experts, E):
+    """Layer output of ``tokens`` from the GPU's own routing (idx, w, pos) and
+    its own FP8 H rows, through the oracle's down GEMM and combine: what the
+    GPU's last two stages must reproduce within the layer tolerance."""
+    T, k = L.idx.shape
+    tokens = np.asarray(tokens)
+    idx = to_np(L.idx)[tokens]; w = to_np(L.w)[tokens]; pos = to_np(L.pos)[tokens]
+    rows = np.concatenate([pos.reshape(-1), T * k + tokens])
+    ids = np.concatenate([idx.reshape(-1), np.full(tokens.size, E)])
+    hq = L.h.index_select(0, torch.as_tensor(rows, device=L.h.device, dtype=torch.long)).cpu().numpy()
+    hs = L.hs.index_select(0, torch.as_tensor(rows, device=L.hs.device, dtype=torch.long)).cpu().numpy()
+    y = oracle_down_rows(hq, hs, ids, experts)
+    n = tokens.size
+    return olayer.combine(y[:n * k].reshape(n, k, -1), w, y[n * k:])
 
 
 def layer_allowance(res, experts, T, k, E, rule="fp32"):
@@ -324,16 +381,25 @@ def layer_allowance(res, experts, T, k, E, rule="fp32"):
 
 
 def token_allowance(extra, r, experts, E, rule="fp32"):
-    """The same bound for tokens evaluated on their own (moe_layer_tokens)."""
+    """The same bound for tokens evaluated on their own (moe_layer_tokens),
+    batched per expert: the (token, slot) rows of one expert share its
+    dequantised W2."""
     n, k = r["idx"].shape
     d = extra["y_shared"].shape[1]
     out = np.zeros((n, d))
+    by_e = {}
     for t in range(n):
-        slots = [(r["idx"][t, j], extra["inter_routed"][(t, j)], abs(float(r["w"][t, j])))
-                 for j in range(k)] + [(E, extra["inter_shared"][t], 1.0)]
-        for e, it, wt in slots:
-            w13q, w13s, w2q, w2s = experts(int(e))
-            amb, sp = h_code_ambiguity(extra["xq"][t:t + 1], extra["xs"][t:t + 1], w13q, w13s,
-                                       it["g"], it["u"], it["h"], it["hs"], rule)
-            out[t] += wt * y_allowance(amb, sp, it["hs"], w2q, w2s)[0]
+        for j in range(k):
+            by_e.setdefault(int(r["idx"][t, j]), []).append((t, extra["inter_routed"][(t, j)],
+                                                            abs(float(r["w"][t, j]))))
+        by_e.setdefault(E, []).append((t, extra["inter_shared"][t], 1.0))
+    for e, items in by_e.items():
+        w13q, w13s, w2q, w2s = experts(e)
+        ts = [t for t, _, _ in items]
+        cat = {key: np.concatenate([it[key] for _, it, _ in items]) for key in ("g", "u", "h", "hs")}
+        amb, sp = h_code_ambiguity(extra["xq"][ts], extra["xs"][ts], w13q, w13s, cat["g"], cat["u"],
+                                   cat["h"], cat["hs"], rule)
+        ya = y_allowance(amb, sp, cat["hs"], w2q, w2s)
+        for i, (t, _, wt) in enumerate(items):
+            out[t] += wt * ya[i]
     return out

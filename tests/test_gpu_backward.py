@@ -127,6 +127,51 @@ def test_combine_backward_quantising(T, k, E, d):
     assert np.array_equal(to_np(dyq), rq) and np.array_equal(to_np(dys), rs)
 
 
+@pytest.mark.parametrize("quantising", [False, True])
+def test_combine_backward_unassigned_slots(quantising):
+    """Slots whose pos lies outside the rows (an unassigned slot, pos = -1, or
+    past the end) get a zero gate gradient and write no dY row (nor its FP8
+    copy); every other row is written as usual."""
+    rng = np.random.default_rng(31)
+    T, k, E, d = 9, 4, 16, 256
+    idx = np.stack([np.sort(rng.choice(E, k, replace=False)) for _ in range(T)])
+    _, pos, _ = operm.permute(idx, E)
+    rows = T * k + T
+    bad = [(3, 1, -1), (5, 2, rows + 7)]
+    freed = [int(pos[t, j]) for t, j, _ in bad]
+    for t, j, v in bad:
+        pos[t, j] = v
+    y = bf16_tensor(rng.standard_normal((rows, d)))
+    dout = bf16_tensor(rng.standard_normal((T, d)))
+    w = rng.uniform(0.05, 1.0, (T, k)).astype(np.float32)
+    sentinel = bf16_tensor(np.full((rows, d), 3.0))
+    dy = sentinel.to(DEV).clone()
+    dw = torch.full((T, k), 7.0, dtype=torch.float32, device=DEV)
+    dyq = torch.full((rows, d), 0x55, dtype=torch.uint8, device=DEV)
+    dys = torch.full((rows, d // 128), 9.0, dtype=torch.float32, device=DEV)
+    if quantising:
+        moe.moe_combine_backward(dout.to(DEV), y.to(DEV), D(pos), D(w), T * k, dy, dw, dyq=dyq, dys=dys)
+    else:
+        moe.moe_combine_backward(dout.to(DEV), y.to(DEV), D(pos), D(w), T * k, dy, dw)
+    torch.cuda.synchronize()
+    gdy, gdw = to_np(dy), to_np(dw)
+    dn = dout.float().numpy()
+    want = sentinel.float().numpy().copy()
+    for t in range(T):
+        for j in range(k):
+            if 0 <= pos[t, j] < rows:
+                want[pos[t, j]] = fp8.bf16_round(fp8.f32(np.float32(w[t, j]) * dn[t].astype(np.float32)))
+        want[T * k + t] = dn[t]
+    assert np.array_equal(gdy, want)
+    for t, j, _ in bad:
+        assert gdw[t, j] == 0.0
+    assert np.all(gdw[gdw != 0.0] != 7.0)
+    for r in freed:
+        assert np.array_equal(gdy[r], sentinel.float().numpy()[r])
+        if quantising:
+            assert torch.all(dyq[r] == 0x55) and torch.all(dys[r] == 9.0)
+
+
 def _routing(rng, T, k, E, empty=()):
     allowed = [e for e in range(E) if e not in empty]
     idx = np.stack([np.sort(rng.choice(allowed, k, replace=False)) for _ in range(T)])

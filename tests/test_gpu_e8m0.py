@@ -16,9 +16,10 @@ import routing_fp8_grouped_amd as moe
 from routing_fp8_grouped_amd import configs, inputs
 from oracle import fp8, quant as oq, route as oroute, layer as olayer
 from oracle.gemm import blocked_gemm
-from tests.gpu_util import (DEV, log, to_np, h_noise, h_code_ambiguity, check_h_codes,
+from tests.gpu_util import (rel_l2_rows, DEV, log, to_np, h_noise, h_code_ambiguity, check_h_codes,
                             pow2_scale_choices, rows_within, device_weights, OracleExperts,
-                            run_layer, layer_allowance, token_allowance)
+                            run_layer, layer_allowance, token_allowance, chain_report,
+                            stage_fed_tokens)
 from tests.test_gpu_kernels import bf16_tensor, random_gemm_shape, varied_activations
 
 pytestmark = pytest.mark.gpu
@@ -203,10 +204,14 @@ def test_tiny_layer_pow2_every_token():
     assert np.array_equal(to_np(L.xq), ref["xq"]) and np.array_equal(to_np(L.xs), ref["xs"])
     for e in range(cfg.E + 1):
         assert np.array_equal(to_np(W.w13s[e]), oe(e)[1]) and np.array_equal(to_np(W.w13q[e]), oe(e)[0])
+    # stage-fed: the GPU's own routing and H through the oracle's last stages
+    sf = stage_fed_tokens(L, np.arange(cfg.T), oe, cfg.E)
+    err_sf = rel_l2_rows(to_np(L.out), sf)
+    log(f"  stage-fed out rel-L2 max {err_sf.max():.2e} median {np.median(err_sf):.2e}")
+    assert np.all(err_sf <= TOL), err_sf.max()
     allow, amb, sp = layer_allowance(ref, oe, cfg.T, cfg.k, cfg.E, rule="pow2")
     okr, err, n_allow = rows_within(to_np(L.out)[ok], ref["out"][ok], allow[ok], TOL)
-    log(f"  out rel-L2 max {err.max():.2e} median {np.median(err):.2e}; "
-        f"rows above {TOL} within the h-code allowance: {n_allow}")
+    log("  " + chain_report(err, rows_within.allow_rel, TOL))
     assert np.all(okr)
 
 
@@ -222,13 +227,17 @@ def test_v3_pow2_sampled_tokens():
     assert np.array_equal(to_np(L.idx)[ok], r["idx"][ok])
     rq, rs = oq.quant_1x128(xn, "pow2")
     assert np.array_equal(to_np(L.xq), rq) and np.array_equal(to_np(L.xs), rs)
-    sample = np.sort(np.random.default_rng(4).choice(np.nonzero(ok)[0], 3, replace=False))
+    sample = np.sort(np.random.default_rng(4).choice(np.nonzero(ok)[0], 64, replace=False))
     oe = OracleExperts(cfg, rule="pow2")
     oe.prepare(sorted(set(r["idx"][sample].reshape(-1).tolist()) | {cfg.E}))
+    sf = stage_fed_tokens(L, sample, oe, cfg.E)
+    err_sf = rel_l2_rows(to_np(L.out)[sample], sf)
+    log(f"  stage-fed out rel-L2 over {sample.size} tokens: max {err_sf.max():.2e} "
+        f"median {np.median(err_sf):.2e}")
+    assert np.all(err_sf <= TOL), err_sf.max()
     out, rs_, extra = olayer.moe_layer_tokens(xn[sample], wg.float().numpy(), b.numpy(), oe, cfg.G,
                                               cfg.M, cfg.k, cfg.route_scale, rule="pow2")
     allow = token_allowance(extra, rs_, oe, cfg.E, rule="pow2")
     okr, err, n_allow = rows_within(to_np(L.out)[sample], out, allow, TOL)
-    log(f"  out rel-L2 on tokens {sample.tolist()}: {np.array2string(err, precision=2)}; "
-        f"above {TOL} within the h-code allowance: {n_allow}")
+    log(f"  {sample.size} tokens, " + chain_report(err, rows_within.allow_rel, TOL))
     assert np.all(okr)

@@ -1,15 +1,27 @@
 """End-to-end parity of the MoE layer (route -> quant -> permute -> grouped GEMM
 -> combine) against the oracle on the five seeded workloads (GPU).
 
-Bar: routing indices, quantised bytes/scales and the permutation bit-exact
-(tokens whose k-th and (k+1)-th biased scores differ by < 1e-6 excluded and
-counted); layer output within relative L2 <= 5e-3 per row, plus, where an
-element of the SwiGLU output h sits within the MFMA's accumulation noise of an
-E4M3 rounding midpoint (two valid codes), the bounded effect of a one-step
-code change (tests/gpu_util.py; the count of rows that needed it is logged).  The tiny workload
-is compared on every token; the V3-shape workloads run in full on the GPU and
-are compared on every token for routing and quantisation and on sampled
-tokens for the output (each token's output depends on that token alone)."""
+Bar (spec: routing indices, quantised bytes/scales and the permutation
+bit-exact outside 1e-6 near ties; relative L2 <= 5e-3 per output row):
+
+* routing, quantisation and permutation bit-exact, near-tie tokens excluded
+  and counted;
+* stage-fed layer output: the GPU's own routing and FP8 H rows run through the
+  oracle's down GEMM and combine; every row within 5e-3 of the GPU's output,
+  with no allowance (near-tie tokens included: the routing is the GPU's);
+* H codes against the oracle's from the same inputs: equal, except where the
+  oracle's h lies within the MFMA's accumulation noise of an E4M3 rounding
+  midpoint (two valid codes; tests/gpu_util.py);
+* independent chain (the GPU layer against the oracle's own chain from x):
+  rows above 5e-3 form a counted category, like near ties, whose size and
+  allowance are printed; each such row must lie within the bounded effect of
+  its ambiguous H codes.
+
+The tiny workload is compared on every token; the V3-shape workloads run in
+full on the GPU and are compared on every token for routing and
+quantisation, and on at least 64 sampled tokens for the output (each token's
+output depends on that token alone).
+"""
 
 import numpy as np
 import pytest
@@ -20,7 +32,7 @@ from routing_fp8_grouped_amd import configs, inputs
 from oracle import quant as oq, route as oroute, permute as operm, layer as olayer
 from tests.gpu_util import (DEV, log, to_np, rel_l2_rows, device_weights, OracleExperts,
                             run_layer, layer_allowance, token_allowance, rows_within,
-                            check_h_codes)
+                            check_h_codes, chain_report, stage_fed_tokens)
 
 pytestmark = pytest.mark.gpu
 TOL = 5e-3
@@ -70,13 +82,18 @@ def test_tiny_layer_every_token():
         assert np.array_equal(to_np(L.pos), ref["pos"])
         assert np.array_equal(to_np(L.row_token)[:cfg.T * cfg.k], ref["row_token"])
     check_permutation_properties(L, gi, cfg.T, cfg.k, cfg.E)
+    # stage-fed: the GPU's H through the oracle's down GEMM and combine, every token
+    sf = stage_fed_tokens(L, np.arange(cfg.T), oe, cfg.E)
+    err_sf = rel_l2_rows(to_np(L.out), sf)
+    log(f"  stage-fed out rel-L2 max {err_sf.max():.2e} median {np.median(err_sf):.2e} "
+        f"over {cfg.T} tokens")
+    assert np.all(err_sf <= TOL), err_sf.max()
     allow, amb, sp = layer_allowance(ref, oe, cfg.T, cfg.k, cfg.E)
     if np.array_equal(gi, r["idx"]):
         n_diff = check_h_codes(to_np(L.h), ref["hq"], amb, sp)
         log(f"  h codes: {int(amb.sum())} ambiguous, {n_diff} differ")
     okr, err, n_allow = rows_within(to_np(L.out)[ok], ref["out"][ok], allow[ok], TOL)
-    log(f"  out rel-L2 max {err.max():.2e} median {np.median(err):.2e}; "
-        f"rows above {TOL} within the h-code allowance: {n_allow}")
+    log("  " + chain_report(err, rows_within.allow_rel, TOL))
     assert np.all(okr)
     # the explicit dispatch copy gives the same bytes as the gathering GEMM
     L2 = run_layer(cfg, x, wg, b, W, dispatch=True)
@@ -125,9 +142,13 @@ def test_degenerate_layers(case):
     if case == "hot_experts":
         assert np.all(to_np(L.idx) == [1, 2, 5, 6])
         assert np.array_equal(to_np(L.offsets), ref["offsets"])
+    sf = stage_fed_tokens(L, np.arange(cfg.T), oe, cfg.E)
+    err_sf = rel_l2_rows(to_np(L.out), sf)
+    log(f"  stage-fed out rel-L2 max {err_sf.max():.2e}")
+    assert np.all(err_sf <= TOL), err_sf.max()
     allow, _, _ = layer_allowance(ref, oe, cfg.T, cfg.k, cfg.E)
     okr, err, n_allow = rows_within(to_np(L.out)[ok], ref["out"][ok], allow[ok], TOL)
-    log(f"  out rel-L2 max {err.max():.2e}; rows above {TOL} within the h-code allowance: {n_allow}")
+    log("  " + chain_report(err, rows_within.allow_rel, TOL))
     assert np.all(okr)
 
 
@@ -166,18 +187,38 @@ def test_v3_workload(name):
         assert np.array_equal(to_np(L.offsets), ro)
         assert np.array_equal(to_np(L.pos), rp)
         assert np.array_equal(to_np(L.row_token)[:cfg.T * cfg.k], rt)
-    # layer output on sampled tokens (not near ties), evaluated by the oracle alone
-    n_s = 3 if cfg.T > 64 else 4
-    cand = np.nonzero(ok)[0]
-    sample = np.sort(np.random.default_rng(2).choice(cand, n_s, replace=False))
+    # layer output on sampled tokens: every token of a decode batch; otherwise
+    # 64 tokens, among them tokens of the most loaded expert and the last token
+    if cfg.T <= 64:
+        sample = np.arange(cfg.T)
+    else:
+        rng = np.random.default_rng(2)
+        hot = int(np.argmax(counts))
+        hot_tokens = np.nonzero(np.any(gi == hot, axis=1))[0]
+        pick = set(rng.choice(hot_tokens, min(8, hot_tokens.size), replace=False).tolist())
+        pick |= {cfg.T - 1, cfg.T - 2}
+        rest = np.setdiff1d(np.arange(cfg.T), sorted(pick))
+        pick |= set(rng.choice(rest, 64 - len(pick), replace=False).tolist())
+        sample = np.array(sorted(pick))
+        log(f"  sample: {sample.size} tokens, {min(8, hot_tokens.size)} of them on expert {hot} "
+            f"({counts[hot]} rows)")
     oe = OracleExperts(cfg)
-    need = sorted(set(r["idx"][sample].reshape(-1).tolist()) | {cfg.E})
-    log(f"  oracle: {len(need)} experts for tokens {sample.tolist()}")
+    need = sorted(set(gi[sample].reshape(-1).tolist()) | set(r["idx"][sample].reshape(-1).tolist())
+                  | {cfg.E})
+    log(f"  oracle: quantising {len(need)} experts")
     oe.prepare(need)
-    out, rs_, extra = olayer.moe_layer_tokens(xn[sample], wg.float().numpy(), b.numpy(), oe, cfg.G,
+    # stage-fed: the GPU's own routing and H rows through the oracle's last stages
+    sf = stage_fed_tokens(L, sample, oe, cfg.E)
+    got = to_np(L.out)[sample]
+    err_sf = rel_l2_rows(got, sf)
+    log(f"  stage-fed out rel-L2 over {sample.size} tokens: max {err_sf.max():.2e} "
+        f"median {np.median(err_sf):.2e}")
+    assert np.all(err_sf <= TOL), err_sf.max()
+    # independent chain on the sampled tokens that are not near ties
+    sample_ok = sample[ok[sample]]
+    out, rs_, extra = olayer.moe_layer_tokens(xn[sample_ok], wg.float().numpy(), b.numpy(), oe, cfg.G,
                                               cfg.M, cfg.k, cfg.route_scale)
     allow = token_allowance(extra, rs_, oe, cfg.E)
-    okr, err, n_allow = rows_within(to_np(L.out)[sample], out, allow, TOL)
-    log(f"  out rel-L2 on sampled tokens: {np.array2string(err, precision=2)}; "
-        f"above {TOL} within the h-code allowance: {n_allow}")
+    okr, err, n_allow = rows_within(to_np(L.out)[sample_ok], out, allow, TOL)
+    log(f"  {sample_ok.size} tokens, " + chain_report(err, rows_within.allow_rel, TOL))
     assert np.all(okr)
