@@ -147,6 +147,23 @@ moe_status moe_permute(const int32_t* idx, int T, int k, int E,
                        uint8_t* xq_perm, float* xs_perm,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_permute_noalloc — moe_permute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and results bit for bit, without the
+ * workspace.  Its per-block histograms live in a static device array of the
+ * library, 1 MiB per GPU (held until the process ends), so
+ * ceil(T/256) * E <= 262144 (T <= 262144 tokens at E = 256); larger calls
+ * return MOE_ERR_UNSUPPORTED.  Allocates nothing (no hipMalloc, hipFree or
+ * allocating library call).  Calls on one GPU share the array: calls that
+ * overlap in time on one GPU (concurrent streams, several host threads) race
+ * and must be serialised by the caller.  Errors as moe_permute, plus
+ * MOE_ERR_HIP if the array's device address cannot be obtained on the
+ * current device. */
+moe_status moe_permute_noalloc(const int32_t* idx, int T, int k, int E,
+                               const uint8_t* xq, const float* xs, int d,
+                               int32_t* offsets, int32_t* pos, int32_t* row_token,
+                               uint8_t* xq_perm, float* xs_perm, void* stream);
+
 /* grouped_gemm_fp8_swiglu — all experts of the layer (summary page section 6;
  * book chapters 7, 16, 17).  For every group g in [0, n_groups) (E routed
  * experts, then the shared expert) and every row r in [offsets[g], offsets[g+1]):

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import MoEError, RouteParams  # noqa: F401
 
 __all__ = ["moe_route", "moe_route_workspace_bytes", "fp8_quant_1x128", "fp8_quant_128x128", "moe_permute_workspace_bytes",
-           "moe_permute", "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up", "grouped_gemm_fp8_down",
+           "moe_permute", "moe_permute_noalloc", "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up", "grouped_gemm_fp8_down",
            "moe_combine", "moe_bias_update", "fp8_quant_1x128_pow2", "fp8_quant_128x128_pow2",
            "grouped_gemm_fp8_up_e8m0", "grouped_gemm_fp8_down_e8m0", "grouped_gemm_fp8_up_train",
            "moe_transpose_fp8_blocks", "moe_combine_backward", "moe_wgrad_columns", "moe_regroup_128x1",
@@ -124,6 +124,24 @@ def moe_permute(idx, n_experts, offsets, pos, row_token, workspace, xq=None, xs=
         _ptr(idx), T, k, n_experts, _ptr(xq), _ptr(xs), d, _ptr(offsets), _ptr(pos),
         _ptr(row_token), _ptr(xq_perm), _ptr(xs_perm), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _stream(stream)))
+
+
+def moe_permute_noalloc(idx, n_experts, offsets, pos, row_token, xq=None, xs=None, xq_perm=None,
+                        xs_perm=None, stream=None):
+    """moe_permute without a workspace: the histograms live in the library's
+    static device array (for callers that cannot allocate; calls that overlap
+    on one GPU race)."""
+    for t, dt, n in ((idx, torch.int32, "idx"), (offsets, torch.int32, "offsets"),
+                     (pos, torch.int32, "pos"), (row_token, torch.int32, "row_token"),
+                     (xq, torch.uint8, "xq"), (xs, torch.float32, "xs"),
+                     (xq_perm, torch.uint8, "xq_perm"), (xs_perm, torch.float32, "xs_perm")):
+        _dev(t, dt, n)
+    T, k = idx.shape
+    d = xq.shape[1] if xq is not None else 0
+    lib = _lib.load()
+    _lib.check("moe_permute_noalloc", lib.moe_permute_noalloc(
+        _ptr(idx), T, k, n_experts, _ptr(xq), _ptr(xs), d, _ptr(offsets), _ptr(pos),
+        _ptr(row_token), _ptr(xq_perm), _ptr(xs_perm), _stream(stream)))
 
 
 def grouped_gemm_fp8_swiglu(aq, as_, row_src, offsets, w13, w13_s, w2, w2_s, h, hs, y, stream=None):

@@ -43,6 +43,7 @@ SIGNATURES = {
     "fp8_quant_128x128": (I, [P, I, I, P, P, P]),
     "moe_permute_workspace_bytes": (SZ, [I, I, I]),
     "moe_permute": (I, [P, I, I, I, P, P, I, P, P, P, P, P, P, SZ, P]),
+    "moe_permute_noalloc": (I, [P, I, I, I, P, P, I, P, P, P, P, P, P]),
     "grouped_gemm_fp8_swiglu": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P, P, P, P]),
     "grouped_gemm_fp8_up": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P]),
     "grouped_gemm_fp8_down": (I, [P, P, P, I, I, I, I, P, P, P, P]),

@@ -208,10 +208,15 @@ size_t moe_permute_workspace_bytes(int T, int k, int E) {
   return moe::permute_workspace_bytes(T, E);
 }
 
-moe_status moe_permute(const int32_t* idx, int T, int k, int E, const uint8_t* xq, const float* xs,
-                       int d, int32_t* offsets, int32_t* pos, int32_t* row_token, uint8_t* xq_perm,
-                       float* xs_perm, void* workspace, size_t workspace_bytes, void* stream) {
-  clear_error();
+}  // extern "C"
+
+namespace {
+
+// Arguments of moe_permute other than the workspace; MOE_OK with T = 0 means
+// nothing is to be done (the caller returns before launching).
+moe_status check_permute(const int32_t* idx, int T, int k, int E, const uint8_t* xq, const float* xs,
+                         int d, int32_t* offsets, int32_t* pos, int32_t* row_token, uint8_t* xq_perm,
+                         float* xs_perm) {
   REQUIRE(T >= 0, "T=%d is negative", T);
   REQUIRE(E >= 1 && E <= 256, "E=%d must be in [1, 256]", E);
   REQUIRE(k >= 1 && k <= 16 && k <= E, "k=%d must be in [1, min(16, E)]", k);
@@ -228,6 +233,19 @@ moe_status moe_permute(const int32_t* idx, int T, int k, int E, const uint8_t* x
     REQUIRE_PTR(xq_perm);
     REQUIRE_PTR4(xs_perm);
   }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_permute(const int32_t* idx, int T, int k, int E, const uint8_t* xq, const float* xs,
+                       int d, int32_t* offsets, int32_t* pos, int32_t* row_token, uint8_t* xq_perm,
+                       float* xs_perm, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  moe_status st = check_permute(idx, T, k, E, xq, xs, d, offsets, pos, row_token, xq_perm, xs_perm);
+  if (st != MOE_OK || T == 0) return st;
   const size_t need = moe::permute_workspace_bytes(T, E);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
@@ -235,6 +253,23 @@ moe_status moe_permute(const int32_t* idx, int T, int k, int E, const uint8_t* x
   return hip_status(moe::launch_permute(idx, T, k, E, xq, xs, d, offsets, pos, row_token, xq_perm,
                                         xs_perm, workspace, static_cast<hipStream_t>(stream)),
                     "moe_permute launch");
+}
+
+moe_status moe_permute_noalloc(const int32_t* idx, int T, int k, int E, const uint8_t* xq,
+                               const float* xs, int d, int32_t* offsets, int32_t* pos,
+                               int32_t* row_token, uint8_t* xq_perm, float* xs_perm, void* stream) {
+  clear_error();
+  moe_status st = check_permute(idx, T, k, E, xq, xs, d, offsets, pos, row_token, xq_perm, xs_perm);
+  if (st != MOE_OK || T == 0) return st;
+  const size_t need = moe::permute_workspace_bytes(T, E);
+  if (need > moe::kPermuteScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "T=%d, E=%d need %zu bytes of scratch; moe_permute_noalloc holds %zu "
+                "(ceil(T/256) * E <= %zu); use moe_permute with a workspace",
+                T, E, need, moe::kPermuteScratchBytes, moe::kPermuteScratchBytes / sizeof(int32_t));
+  return hip_status(moe::launch_permute_noalloc(idx, T, k, E, xq, xs, d, offsets, pos, row_token,
+                                                xq_perm, xs_perm, static_cast<hipStream_t>(stream)),
+                    "moe_permute_noalloc");
 }
 
 namespace {

@@ -23,6 +23,13 @@ hipError_t launch_route_ws(const uint16_t* x, const uint16_t* wg, const float* b
                            hipStream_t stream);
 
 size_t permute_workspace_bytes(int T, int E);
+// Largest workspace the allocation-free permute holds in its static device
+// array (per-block histograms: ceil(T/256) * E int32).
+constexpr size_t kPermuteScratchBytes = size_t(1) << 20;
+hipError_t launch_permute_noalloc(const int32_t* idx, int T, int k, int E, const uint8_t* xq,
+                                  const float* xs, int d, int32_t* offsets, int32_t* pos,
+                                  int32_t* row_token, uint8_t* xq_perm, float* xs_perm,
+                                  hipStream_t stream);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const uint8_t* xq,
                           const float* xs, int d, int32_t* offsets, int32_t* pos,
                           int32_t* row_token, uint8_t* xq_perm, float* xs_perm, void* ws,

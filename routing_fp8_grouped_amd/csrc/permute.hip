@@ -14,6 +14,8 @@
 // and an optional gather that copies each token's FP8 row and scales to its
 // k + 1 rows (the dispatch proper; the grouped GEMM can instead read the
 // token rows through row_token).
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -156,6 +158,51 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, const uint8_t
                        xq, xs, T, d, xq_perm, xs_perm);
   }
   return hipGetLastError();
+}
+
+// ---- allocation-free variant ----
+// The per-block histograms of moe_permute_noalloc live in a file-scope device
+// array of kPermuteScratchBytes, one copy per GPU for the life of the process.
+// Host code never passes the array's name to a kernel (on the host it only
+// stands for the symbol): the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and that pointer is what
+// the kernels receive.  The count kernel overwrites every entry a call uses,
+// so nothing is cleared between calls; calls that overlap on one GPU share
+// the array and race.
+static __device__ __align__(256) int32_t scratch[kPermuteScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each GPU
+}  // namespace
+
+static hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_permute_noalloc(const int32_t* idx, int T, int k, int E, const uint8_t* xq,
+                                  const float* xs, int d, int32_t* offsets, int32_t* pos,
+                                  int32_t* row_token, uint8_t* xq_perm, float* xs_perm,
+                                  hipStream_t stream) {
+  if (permute_workspace_bytes(T, E) > kPermuteScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_permute(idx, T, k, E, xq, xs, d, offsets, pos, row_token, xq_perm, xs_perm, ws, stream);
 }
 
 }  // namespace moe

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(lib):
     declared = _lib.header_symbols()
     assert set(declared) == {"moe_route", "moe_route_workspace_bytes", "moe_route_ws",
                              "fp8_quant_1x128", "fp8_quant_128x128",
-                             "moe_permute_workspace_bytes", "moe_permute",
+                             "moe_permute_workspace_bytes", "moe_permute", "moe_permute_noalloc",
                              "grouped_gemm_fp8_swiglu", "grouped_gemm_fp8_up",
                              "grouped_gemm_fp8_down", "moe_combine", "moe_bias_update",
                              "fp8_quant_1x128_pow2", "fp8_quant_128x128_pow2",
@@ -231,3 +231,19 @@ def test_backward_validation(lib):
     assert lib.grouped_gemm_fp8_wgrad(A, A, A, A, A, 3, 100, 256, 256, MIS, None) == 1
     up = lambda gu=A: lib.grouped_gemm_fp8_up_train(A, A, 10, A, A, 257, 100, 256, 128, A, A, A, A, gu, A, None)
     assert up(gu=None) == 1 and "gu is NULL" in last(lib)
+
+
+def test_permute_noalloc_validation(lib):
+    """The allocation-free permute validates like moe_permute and refuses
+    sizes beyond its static scratch (1 MiB: ceil(T/256) * E <= 262144) before
+    any GPU call."""
+    # T = 262145 at E = 256: 1025 blocks of histograms, 1,049,600 bytes
+    st = lib.moe_permute_noalloc(A, 262145, 8, 256, None, None, 0, A, A, A, None, None, None)
+    assert st == 2 and "moe_permute with a workspace" in last(lib)
+    st = lib.moe_permute_noalloc(A, 100000, 8, 300, None, None, 0, A, A, A, None, None, None)
+    assert st == 1 and "E=300" in last(lib)
+    st = lib.moe_permute_noalloc(None, 16, 8, 256, None, None, 0, A, A, A, None, None, None)
+    assert st == 1 and "idx" in last(lib)
+    st = lib.moe_permute_noalloc(A, 16, 8, 256, None, None, 0, A, A, MIS4, None, None, None)
+    assert st == 1 and "row_token" in last(lib)
+    assert lib.moe_permute_noalloc(A, 0, 8, 256, None, None, 0, None, None, None, None, None, None) == 0
