@@ -191,6 +191,86 @@ def timed_backward(layer, dout, Wt, steps):
     return (t1 - t0) * 1e3 / steps, stage_ms
 
 
+def measured_roofs(reps=5):
+    """The FP8 MFMA issue rate and the HBM read rate this GPU sustains, from
+    the library's two measurement kernels (moe_roof_fp8_mfma,
+    moe_roof_hbm_read), timed with HIP events on the launch stream; the median
+    of ``reps`` runs."""
+    import ctypes
+    lib = moe._lib.load()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg_mfma, iters = 2 * cus, 20000
+    sink = torch.empty(max(wg_mfma, 8 * cus) * 256, dtype=torch.float32, device="cuda")
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")     # 16x the last-level cache
+    buf.fill_(1)
+
+    def timed(call):
+        ms = []
+        for _ in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            moe._lib.check("roof", call())
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return float(np.median(ms[1:]))     # the first run warms up
+
+    ms_mfma = timed(lambda: lib.moe_roof_fp8_mfma(wg_mfma, iters, ctypes.c_void_p(sink.data_ptr()), sp))
+    flop = wg_mfma * 4 * iters * 8 * 65536
+    ms_read = timed(lambda: lib.moe_roof_hbm_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), 2 * cus,
+                                                  ctypes.c_void_p(sink.data_ptr()), sp))
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"fp8_mfma_tflops": flop / (ms_mfma * 1e-3) / 1e12,
+            "hbm_read_gbs": (4 << 30) / (ms_read * 1e-3) / 1e9,
+            "note": "moe_roof_fp8_mfma: 8 independent FP8 MFMA chains per wave, no memory traffic, "
+                    f"{wg_mfma} workgroups x 4 waves; moe_roof_hbm_read: non-temporal 16-byte loads over "
+                    f"a 4 GiB buffer, a contiguous share per workgroup, {2 * cus} workgroups; median of "
+                    f"{reps} runs each"}
+
+
+def decode_leg(W, roofs, steps, warmup):
+    """The decode workload (64 tokens at the V3 shape) on the same resident FP8
+    weights: layer time, the HBM rate of the bytes the method must move, and
+    the roofline of its dominant kernel (the first expert GEMM, HBM-bound)."""
+    cfg = configs.get("decode_64")
+    x, wg, b = (t.cuda() for t in inputs.host_inputs(cfg))
+    layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.f, cfg.route_scale)
+    for _ in range(warmup):
+        layer.forward(x, wg, b, W)
+    torch.cuda.synchronize()
+    ms, st = timed_steps(layer, x, wg, b, W, steps)
+    counts = np.bincount(layer.idx.cpu().numpy().reshape(-1), minlength=cfg.E)
+    touched = int((counts > 0).sum()) + 1
+    d, f = cfg.d, cfg.f
+    w13_b = 2 * f * d + (2 * f // 128) * (d // 128) * 4
+    w2_b = d * f + (d // 128) * (f // 128) * 4
+    layer_bytes = touched * (w13_b + w2_b) + cfg.E * d * 2 + cfg.E * 4 + 2 * cfg.T * d * 2
+    up_bytes = touched * w13_b + cfg.T * (d + d // 128 * 4) + cfg.rows * (f + f // 128 * 4)
+    up_s = st["gemm_up"] * 1e-3
+    layer_gbs = layer_bytes / (ms * 1e-3) / 1e9
+    up_gbs = up_bytes / up_s / 1e9
+    log(f"decode_64: {ms:.3f} ms/step, {touched} experts touched, layer {layer_gbs:.0f} GB/s; stages " +
+        ", ".join(f"{k} {v:.3f}" for k, v in st.items()))
+    return {
+        "workload": cfg.name, "tokens": cfg.T, "ms_per_step": ms, "tokens_per_s": cfg.T / (ms * 1e-3),
+        "stages_ms": st, "experts_touched": touched, "algorithmic_bytes": layer_bytes,
+        "hbm_gbs": layer_gbs, "hbm_frac_of_peak": layer_gbs / HBM_PEAK_GBS,
+        "hbm_frac_of_measured": layer_gbs / roofs["hbm_read_gbs"],
+        "roofline": {"bound": "hbm", "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": up_gbs / HBM_PEAK_GBS, "measured_peak": roofs["hbm_read_gbs"],
+                     "frac_of_measured": up_gbs / roofs["hbm_read_gbs"],
+                     "kernel": "grouped_gemm_fp8_up (grouped_gemm_small_kernel<true, false>)",
+                     "algorithmic_bytes_per_launch": up_bytes, "avg_launch_ms": st["gemm_up"],
+                     "traffic": read_traffic(cfg.name, profiling.STREAMING)},
+        "note": "algorithmic bytes: each touched expert's W1, W3, W2 codes and scales once, the "
+                "router weights, the token rows in and the output out; the same resident weights "
+                "as the headline workload (same shapes and distribution)",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +284,8 @@ def main():
     ap.add_argument("--no-e8m0", action="store_true",
                     help="skip the timing of the power-of-two (E8M0) scale variant")
     ap.add_argument("--no-backward", action="store_true", help="skip the timing of the backward")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode_64 leg")
+    ap.add_argument("--no-roofs", action="store_true", help="skip the measured roofs")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -269,6 +351,12 @@ def main():
         roof = {"bound": "hbm", "achieved": up_bytes / up_s / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    roofs = None if args.no_roofs else measured_roofs()
+    if roofs is not None:
+        log(f"measured roofs: FP8 MFMA {roofs['fp8_mfma_tflops']:.0f} TFLOP/s, "
+            f"HBM read {roofs['hbm_read_gbs']:.0f} GB/s")
+        roof["measured_peak"] = roofs["fp8_mfma_tflops"] if roof["bound"] == "mfma" else roofs["hbm_read_gbs"]
+        roof["frac_of_measured"] = roof["achieved"] / roof["measured_peak"]
 
     result = {
         "metric": METRIC,
@@ -303,6 +391,11 @@ def main():
         "context": "pages: 2.788M H800 GPU-hours for the whole V3 training run; "
                    "180K H800 GPU-hours per trillion training tokens (not comparable)",
     }
+    if roofs is not None:
+        result["measured_roofs"] = roofs
+    if not args.no_decode and cfg.name != "decode_64":
+        result["decode"] = decode_leg(W, roofs or {"hbm_read_gbs": float("nan")}, args.steps,
+                                      args.warmup)
     if not args.no_backward:
         Wt = W.transposed()
         layer.forward(x, wg, b, W, train=True)

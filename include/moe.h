@@ -389,6 +389,24 @@ moe_status grouped_gemm_fp8_wgrad(const uint8_t* a_t, const float* a_ts, const u
                                   const float* b_ts, const int32_t* offsets, int n_groups,
                                   int total_rows, int M, int N, float* dw, void* stream);
 
+/* Measurement utilities (not steps of the layer): the two roofs the layer's
+ * kernels are bound by, measured on the device, to read a kernel's rate
+ * against beside the datasheet peaks (5.0 PFLOP/s dense FP8, 8 TB/s).
+ *
+ * moe_roof_fp8_mfma — `workgroups` workgroups of 4 waves; every wave issues
+ *   iters * 8 FP8 MFMAs (v_mfma_scale_f32_16x16x128_f8f6f4, 65536 FLOP each)
+ *   back to back on 8 independent accumulators, operands in registers, no
+ *   memory traffic: workgroups * 4 * iters * 8 * 65536 FLOP per call.
+ *   sink [workgroups * 256] FP32 out (each thread's accumulator sum).
+ * moe_roof_hbm_read — reads every byte of buf [bytes] (16-byte aligned,
+ *   bytes % 16 == 0) once with 16-byte loads from `workgroups` workgroups of
+ *   256 threads; sink [workgroups * 256] uint32 out (an XOR of the words each
+ *   thread read).  Use a buffer much larger than the 256 MB last-level cache.
+ * Both: asynchronous on `stream`; the caller times them (HIP events). */
+moe_status moe_roof_fp8_mfma(int workgroups, int iters, float* sink, void* stream);
+moe_status moe_roof_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
+                             void* stream);
+
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 

@@ -44,6 +44,8 @@ SIGNATURES = {
     "moe_permute_workspace_bytes": (SZ, [I, I, I]),
     "moe_permute": (I, [P, I, I, I, P, P, I, P, P, P, P, P, P, SZ, P]),
     "moe_permute_noalloc": (I, [P, I, I, I, P, P, I, P, P, P, P, P, P]),
+    "moe_roof_fp8_mfma": (I, [I, I, P, P]),
+    "moe_roof_hbm_read": (I, [P, SZ, I, P, P]),
     "grouped_gemm_fp8_swiglu": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P, P, P, P]),
     "grouped_gemm_fp8_up": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P]),
     "grouped_gemm_fp8_down": (I, [P, P, P, I, I, I, I, P, P, P, P]),

@@ -611,4 +611,24 @@ moe_status moe_bias_update(const int32_t* offsets, int n_experts, float gamma, f
                     "moe_bias_update launch");
 }
 
+moe_status moe_roof_fp8_mfma(int workgroups, int iters, float* sink, void* stream) {
+  clear_error();
+  REQUIRE(workgroups >= 1 && workgroups <= (1 << 20), "workgroups=%d must be in [1, 2^20]", workgroups);
+  REQUIRE(iters >= 1, "iters=%d must be >= 1", iters);
+  REQUIRE_PTR4(sink);
+  return hip_status(moe::launch_roof_mfma(workgroups, iters, sink, static_cast<hipStream_t>(stream)),
+                    "moe_roof_fp8_mfma launch");
+}
+
+moe_status moe_roof_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
+                             void* stream) {
+  clear_error();
+  REQUIRE(workgroups >= 1 && workgroups <= (1 << 20), "workgroups=%d must be in [1, 2^20]", workgroups);
+  REQUIRE(bytes >= 16 && bytes % 16 == 0, "bytes=%zu must be a positive multiple of 16", bytes);
+  REQUIRE_PTR(buf);
+  REQUIRE_PTR4(sink);
+  return hip_status(moe::launch_roof_read(buf, bytes, workgroups, sink, static_cast<hipStream_t>(stream)),
+                    "moe_roof_hbm_read launch");
+}
+
 }  // extern "C"

@@ -44,15 +44,49 @@ struct SmallArgs {
   uint16_t* y;
 };
 
-struct Frag3 {
-  v8i a, b0, b1;
-};
-
 __device__ __forceinline__ v8i load_frag(const uint8_t* p) {
   const uint4 lo = *reinterpret_cast<const uint4*>(p);
   const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
+
+// Weight fragments are loaded as whole 128-byte lines: for a fragment of 16
+// weight rows R .. R+15 (one K block), lane (g, j) (g = lane / 16, j = lane % 16)
+// loads 16 bytes of chunk c = 2g + (j >= 8) from row R + j % 8 (load x) and from
+// row R + 8 + j % 8 (load y), so each load instruction reads 8 rows entirely,
+// with non-temporal loads (the weights are read once per launch).  Streaming
+// whole lines this way is faster than the fragment's own layout, in which a
+// line is split between two instructions.  Two DPP moves per register
+// (rotate each 16-lane row by 8, write only half of its lanes) then give lane
+// (g, j) chunks 2g and 2g + 1 of row R + j, the MFMA's operand layout:
+//   frag lo = x, with lanes 8..15 of each row taken from y's lanes 0..7
+//   frag hi = y, with lanes 0..7 of each row taken from x's lanes 8..15
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+struct LinePair {
+  i32x4 x, y;
+};
+
+__device__ __forceinline__ LinePair load_lines(const uint8_t* x_src, const uint8_t* y_src) {
+  return {__builtin_nontemporal_load(reinterpret_cast<const i32x4*>(x_src)),
+          __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(y_src))};
+}
+
+__device__ __forceinline__ v8i lines_to_frag(const LinePair& l) {
+  constexpr int ROW_ROR8 = 0x128;
+  v8i f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = __builtin_amdgcn_update_dpp(l.x[i], l.y[i], ROW_ROR8, 0xF, 0xC, false);
+    f[4 + i] = __builtin_amdgcn_update_dpp(l.y[i], l.x[i], ROW_ROR8, 0xF, 0x3, false);
+  }
+  return f;
+}
+
+struct Frag3 {
+  v8i a;
+  LinePair b0, b1;
+};
 
 // POW2: H is requantised with the power-of-two scale rule (the variant whose
 // scales are all powers of two; with such scales the promotion is exact).
@@ -148,11 +182,17 @@ __global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
     }
     const bool col0_ok = SWIGLU || wr0 - r16 < p.N;
     const bool col1_ok = SWIGLU || wr1 - r16 < p.N;
-    wr0 = min(wr0, p.N - 1);
-    wr1 = min(wr1, p.N - 1);
+    // whole-line loads: this lane reads chunk 2 g16 + (r16 >= 8) of rows
+    // base + r16 % 8 and base + 8 + r16 % 8 of each fragment (rows past the
+    // group's weights, in a partial last block, read its last row instead;
+    // their columns are never stored)
     const uint8_t* gb_ = p.b + (size_t)g * p.N * p.K;
-    const uint8_t* pb0 = gb_ + (size_t)wr0 * p.K + g16 * 32;
-    const uint8_t* pb1 = gb_ + (size_t)wr1 * p.K + g16 * 32;
+    const int lr = r16 & 7, lc = (2 * g16 + (r16 >> 3)) * 16;
+    const int fb0 = wr0 - r16, fb1 = wr1 - r16;
+    const uint8_t* pb0x = gb_ + (size_t)min(fb0 + lr, p.N - 1) * p.K + lc;
+    const uint8_t* pb0y = gb_ + (size_t)min(fb0 + 8 + lr, p.N - 1) * p.K + lc;
+    const uint8_t* pb1x = gb_ + (size_t)min(fb1 + lr, p.N - 1) * p.K + lc;
+    const uint8_t* pb1y = gb_ + (size_t)min(fb1 + 8 + lr, p.N - 1) * p.K + lc;
     // stage 2: waves 0..3 lie in weight-scale block 2n, waves 4..7 in 2n+1
     const int swc0 = SWIGLU ? 0 : (wave >= 4 ? 1 : 0);
     const int swc1 = SWIGLU ? 1 : swc0;
@@ -163,8 +203,8 @@ __global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
     for (int j = 0; j < SM_D; ++j) {
       if (j < KB) {
         buf[j].a = load_frag(pa + j * 128);
-        buf[j].b0 = load_frag(pb0 + j * 128);
-        buf[j].b1 = load_frag(pb1 + j * 128);
+        buf[j].b0 = load_lines(pb0x + j * 128, pb0y + j * 128);
+        buf[j].b1 = load_lines(pb1x + j * 128, pb1y + j * 128);
       }
     }
     for (int kb0 = 0; kb0 < KB; kb0 += SM_D) {
@@ -172,12 +212,13 @@ __global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
       for (int j = 0; j < SM_D; ++j) {
         const int kb = kb0 + j;
         if (kb < KB) {
-          const v4f p0 = mfma_fp8_16x16x128(buf[j].a, buf[j].b0, v4f{0.f, 0.f, 0.f, 0.f});
-          const v4f p1 = mfma_fp8_16x16x128(buf[j].a, buf[j].b1, v4f{0.f, 0.f, 0.f, 0.f});
+          const v4f p0 = mfma_fp8_16x16x128(buf[j].a, lines_to_frag(buf[j].b0), v4f{0.f, 0.f, 0.f, 0.f});
+          const v4f p1 = mfma_fp8_16x16x128(buf[j].a, lines_to_frag(buf[j].b1), v4f{0.f, 0.f, 0.f, 0.f});
           if (kb + SM_D < KB) {
-            buf[j].a = load_frag(pa + (kb + SM_D) * 128);
-            buf[j].b0 = load_frag(pb0 + (kb + SM_D) * 128);
-            buf[j].b1 = load_frag(pb1 + (kb + SM_D) * 128);
+            const int o = (kb + SM_D) * 128;
+            buf[j].a = load_frag(pa + o);
+            buf[j].b0 = load_lines(pb0x + o, pb0y + o);
+            buf[j].b1 = load_lines(pb1x + o, pb1y + o);
           }
           const float4 sa = *reinterpret_cast<const float4*>(&sSA[kb][g16 * 4]);
           const float s0 = sSW[swc0][kb], s1 = sSW[swc1][kb];

@@ -81,4 +81,9 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
                           int d, int shared_row0, const uint16_t* residual, uint16_t* out,
                           hipStream_t stream);
 
+// Measured roofs (roofs.hip): FP8 MFMA issue rate and HBM read streaming.
+hipError_t launch_roof_mfma(int workgroups, int iters, float* sink, hipStream_t stream);
+hipError_t launch_roof_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
+                            hipStream_t stream);
+
 }  // namespace moe

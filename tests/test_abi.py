@@ -36,6 +36,7 @@ def test_exports_every_declared_symbol(lib):
                              "moe_combine_backward", "moe_combine_backward_q",
                              "moe_wgrad_columns", "moe_regroup_128x1",
                              "moe_swiglu_backward", "grouped_gemm_fp8_wgrad",
+                             "moe_roof_fp8_mfma", "moe_roof_hbm_read",
                              "moe_status_string", "moe_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -247,3 +248,11 @@ def test_permute_noalloc_validation(lib):
     st = lib.moe_permute_noalloc(A, 16, 8, 256, None, None, 0, A, A, MIS4, None, None, None)
     assert st == 1 and "row_token" in last(lib)
     assert lib.moe_permute_noalloc(A, 0, 8, 256, None, None, 0, None, None, None, None, None, None) == 0
+
+
+def test_roof_validation(lib):
+    assert lib.moe_roof_fp8_mfma(0, 10, A, None) == 1
+    assert lib.moe_roof_fp8_mfma(4, 0, A, None) == 1
+    assert lib.moe_roof_fp8_mfma(4, 10, None, None) == 1 and "sink" in last(lib)
+    assert lib.moe_roof_hbm_read(A, 24, 4, A, None) == 1 and "bytes" in last(lib)
+    assert lib.moe_roof_hbm_read(MIS, 32, 4, A, None) == 1 and "buf" in last(lib)
