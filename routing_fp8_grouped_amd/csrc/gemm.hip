@@ -603,7 +603,7 @@ hipError_t launch_gemm_up(const uint8_t* aq, const float* as, int a_rows, const 
                           bool e8m0, hipStream_t stream, uint8_t* gu, float* gus) {
   // few rows per group: stream the weights (the tiled kernel alone writes the
   // [G, U] cache)
-  if (total_rows <= 16 * n_groups && gu == nullptr)
+  if (total_rows <= 16 * n_groups && gu == nullptr && d <= kSmallMaxK)
     return launch_gemm_up_small(aq, as, a_rows, row_src, offsets, n_groups, total_rows, d, f, w13,
                                 w13_s, h, hs, e8m0, stream);
   const int grid = ((num_cus() + 7) / 8) * 8;
@@ -636,7 +636,7 @@ hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* of
                             uint16_t* y, bool e8m0, hipStream_t stream) {
   // few rows per group: the weight-streaming kernel, whose software promotion
   // is exact with power-of-two scales
-  if (total_rows <= 16 * n_groups)
+  if (total_rows <= 16 * n_groups && f <= kSmallMaxK)
     return launch_gemm_down_small(h, hs, offsets, n_groups, total_rows, d, f, w2, w2_s, y, stream);
   const int grid = ((num_cus() + 7) / 8) * 8;
   GemmArgs s2{};

@@ -7,8 +7,10 @@
 // A tile is at most 16 rows of one group (an "m-chunk") against 256 weight
 // rows.  Each of the 8 waves owns 32 weight rows and streams their FP8 codes
 // from global memory straight into registers, SM_D K blocks ahead, with no
-// LDS ring and no barrier inside the K loop; it reads the tile's 16 activation
-// rows the same way (they are shared by the waves and stay in L2).  In stage 1
+// LDS ring and no barrier inside the K loop.  The tile's 16 activation rows
+// (shared by the waves and by every weight block of the group, so they come
+// from L2) are staged in LDS once per tile, which keeps the memory pipeline
+// for the weight stream; this bounds K at kSmallMaxK.  In stage 1
 // wave w owns the gate rows w*16 .. +15 and the matching up rows, so SiLU(g)*u
 // is formed in registers; the 1x128 amax across the 8 waves goes through LDS.
 // Scales: the rows' activation scales and the two weight-scale columns of the
@@ -22,8 +24,9 @@ namespace moe {
 
 constexpr int SM_M = 16;          // rows per m-chunk
 constexpr int SM_THREADS = 512;   // 8 waves
-constexpr int SM_D = 6;           // K blocks of loads in flight per wave
-constexpr int SM_MAX_KB = 128;    // K <= 16384
+constexpr int SM_D = 4;           // K blocks of weight loads in flight per wave
+constexpr int SM_MAX_KB = kSmallMaxK / 128;
+constexpr int SM_AROW = kSmallMaxK + 16;   // LDS bytes per staged activation row (padded)
 constexpr int SM_MAX_GROUPS = 1024;
 
 struct SmallArgs {
@@ -43,12 +46,6 @@ struct SmallArgs {
   float* hs;
   uint16_t* y;
 };
-
-__device__ __forceinline__ v8i load_frag(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
 
 // Weight fragments are loaded as whole 128-byte lines: for a fragment of 16
 // weight rows R .. R+15 (one K block), lane (g, j) (g = lane / 16, j = lane % 16)
@@ -83,10 +80,19 @@ __device__ __forceinline__ v8i lines_to_frag(const LinePair& l) {
   return f;
 }
 
-struct Frag3 {
-  v8i a;
+struct Frag2 {
   LinePair b0, b1;
 };
+
+// Activation fragment of row r16, K bytes kb*128 + g16*32 .. +31, from the
+// tile's rows staged in LDS (row stride SM_AROW: consecutive rows start 16
+// bytes apart in the banks, so the 16 rows of a read hit different banks).
+__device__ __forceinline__ v8i lds_frag(const uint8_t* sA, int r16, int g16, int kb) {
+  const uint8_t* q = sA + r16 * SM_AROW + kb * 128 + g16 * 32;
+  const uint4 lo = *reinterpret_cast<const uint4*>(q);
+  const uint4 hi = *reinterpret_cast<const uint4*>(q + 16);
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
 
 // POW2: H is requantised with the power-of-two scale rule (the variant whose
 // scales are all powers of two; with such scales the promotion is exact).
@@ -98,6 +104,7 @@ __global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
   __shared__ float sSW[2][SM_MAX_KB];              // weight scales of column sets 0 / 1
   __shared__ float sAmax[SM_THREADS / 64][SM_M];
   __shared__ int sRow[SM_M];
+  __shared__ __attribute__((aligned(16))) uint8_t sA[SM_M * SM_AROW];   // the tile's activation rows
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -166,12 +173,22 @@ __global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
       else sb = min(2 * n + c, nsb - 1);
       sSW[c][kb] = p.bs[(size_t)(g * nsb + sb) * KB + kb];
     }
+    // the tile's 16 activation rows, once per tile (they come from L2: every
+    // weight block of the group reads the same rows); the waves then read
+    // their fragments from LDS instead of each loading them per K block
+    {
+      const int c16 = p.K / 16;
+      for (int i = tid; i < SM_M * c16; i += SM_THREADS) {
+        const int r = i / c16, c = i - r * c16;
+        *reinterpret_cast<uint4*>(&sA[r * SM_AROW + c * 16]) =
+            *reinterpret_cast<const uint4*>(p.a + (size_t)sRow[r] * p.K + c * 16);
+      }
+    }
     __syncthreads();
 
-    // ---- this wave's operands: activation row sRow[r16]; weight rows of the
-    // two 16-column blocks (stage 1: gate and up of h columns wave*16 .. +15;
+    // ---- this wave's operands: activation row r16 of the tile (in LDS); weight
+    // rows of the two 16-column blocks (stage 1: gate and up of h columns wave*16 .. +15;
     // stage 2: rows wave*32 .. +31 of the 256-row block) ----
-    const uint8_t* pa = p.a + (size_t)sRow[r16] * p.K + g16 * 32;
     int wr0, wr1;
     if (SWIGLU) {
       wr0 = n * 128 + wave * 16 + r16;
@@ -198,25 +215,26 @@ __global__ __launch_bounds__(SM_THREADS, 1) void grouped_gemm_small_kernel(
     const int swc1 = SWIGLU ? 1 : swc0;
 
     v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
-    Frag3 buf[SM_D];
+    Frag2 buf[SM_D];
 #pragma unroll
     for (int j = 0; j < SM_D; ++j) {
       if (j < KB) {
-        buf[j].a = load_frag(pa + j * 128);
         buf[j].b0 = load_lines(pb0x + j * 128, pb0y + j * 128);
         buf[j].b1 = load_lines(pb1x + j * 128, pb1y + j * 128);
       }
     }
+    v8i a_next = lds_frag(sA, r16, g16, 0);
     for (int kb0 = 0; kb0 < KB; kb0 += SM_D) {
 #pragma unroll
       for (int j = 0; j < SM_D; ++j) {
         const int kb = kb0 + j;
         if (kb < KB) {
-          const v4f p0 = mfma_fp8_16x16x128(buf[j].a, lines_to_frag(buf[j].b0), v4f{0.f, 0.f, 0.f, 0.f});
-          const v4f p1 = mfma_fp8_16x16x128(buf[j].a, lines_to_frag(buf[j].b1), v4f{0.f, 0.f, 0.f, 0.f});
+          const v8i af = a_next;
+          if (kb + 1 < KB) a_next = lds_frag(sA, r16, g16, kb + 1);
+          const v4f p0 = mfma_fp8_16x16x128(af, lines_to_frag(buf[j].b0), v4f{0.f, 0.f, 0.f, 0.f});
+          const v4f p1 = mfma_fp8_16x16x128(af, lines_to_frag(buf[j].b1), v4f{0.f, 0.f, 0.f, 0.f});
           if (kb + SM_D < KB) {
             const int o = (kb + SM_D) * 128;
-            buf[j].a = load_frag(pa + o);
             buf[j].b0 = load_lines(pb0x + o, pb0y + o);
             buf[j].b1 = load_lines(pb1x + o, pb1y + o);
           }

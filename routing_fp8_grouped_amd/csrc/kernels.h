@@ -44,7 +44,9 @@ hipError_t launch_gemm_down(const uint8_t* h, const float* hs, const int32_t* of
                             uint16_t* y, bool e8m0, hipStream_t stream);
 
 // Variants of the two expert GEMMs for few rows per group (weight streaming;
-// launch_gemm_up/down choose them when total_rows <= 16 * n_groups).
+// launch_gemm_up/down choose them when total_rows <= 16 * n_groups and K is at
+// most kSmallMaxK, the activation rows they stage in LDS).
+constexpr int kSmallMaxK = 7168;
 hipError_t launch_gemm_up_small(const uint8_t* aq, const float* as, int a_rows,
                                 const int32_t* row_src, const int32_t* offsets, int n_groups,
                                 int total_rows, int d, int f, const uint8_t* w13,

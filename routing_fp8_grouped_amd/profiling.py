@@ -58,6 +58,8 @@ KERNELS = {
     "permute_gather": "moe_permute (gather)",
     "combine_kernel": "moe_combine",
     "bias_update_kernel": "moe_bias_update",
+    "roof_mfma_kernel": "moe_roof_fp8_mfma",
+    "roof_read_kernel": "moe_roof_hbm_read",
 }
 GIB_KIB = float(1 << 20)
 
