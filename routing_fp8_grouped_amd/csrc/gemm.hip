@@ -468,6 +468,10 @@ __device__ __forceinline__ void k_block(v4f (&acc)[4][8], Frags& F, Loader<SWIGL
         }
       } else {
         part[i % (PD + 1)] = mfma_fp8_16x16x128(F.bq[ns & 1], F.af[ms], v4f{0.f, 0.f, 0.f, 0.f});
+        // MFMA i is issued before the promotion of partial i - PD (the
+        // compiler would otherwise move the promotion up to its own MFMA and
+        // stall the wave for that MFMA's latency)
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (!E8M0 && i >= PD) {
         const int pi = i - PD, pms = pi & 3, pns = pi >> 2;

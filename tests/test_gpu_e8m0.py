@@ -124,6 +124,9 @@ def _weights(experts, d, f):
     ([3, 0, 200, 64], 384, 256, True),
     ([129, 5], 512, 384, False),
     ([300, 520, 17], 7168, 2048, True),
+    # 17 .. 192 rows per group (partial tiles)
+    ([17, 192, 0, 100, 193], 640, 256, True),
+    ([150, 64, 190], 7168, 2048, True),
     # at most 16 rows per group on average: the weight-streaming kernels
     ([2, 1, 3], 7168, 2048, True),
     ([0, 3, 16, 17, 1, 0], 384, 256, True),

@@ -244,6 +244,12 @@ def gemm_case(rng, counts, d, f, a_rows, gather):
     ([3, 0, 200, 64], 384, 256, True),
     ([129, 5], 512, 384, False),
     ([300, 520, 17], 7168, 2048, True),     # the V3 shape on the tiled kernel
+    # 17 .. 192 rows per group (prefill sizes): partial 256-row tiles whose
+    # waves past the group's end skip the multiply, an empty group, a partial
+    # 256-row block of W2 at d = 640, K = 7168 with 56 promotions
+    ([17, 192, 0, 100, 193], 640, 256, True),
+    ([150, 64, 190], 7168, 2048, True),
+    ([40, 33], 128, 384, False),
     # at most 16 rows per group on average: the weight-streaming kernels
     # (chunks of 16 rows, a partial 256-row block of W2 at d = 384)
     ([2, 1, 3], 7168, 2048, True),
