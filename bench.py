@@ -206,7 +206,7 @@ def measured_roofs(reps=5):
     buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")     # 16x the last-level cache
     buf.fill_(1)
 
-    def timed(call):
+    def timed(call, reps=reps):
         ms = []
         for _ in range(reps + 1):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -221,14 +221,57 @@ def measured_roofs(reps=5):
     flop = wg_mfma * 4 * iters * 8 * 65536
     ms_read = timed(lambda: lib.moe_roof_hbm_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), 2 * cus,
                                                   ctypes.c_void_p(sink.data_ptr()), sp))
-    del buf, sink
+    # the expert GEMMs' weight-load pattern (rows of 7168 bytes, direct loads
+    # into per-wave LDS rings, one workgroup of 8 waves per CU) with 1, 2 and
+    # 4 blocks of 4 KB in flight per wave
+    K = 7168
+    dma_bytes = (buf.numel() // (32 * K)) * 32 * K
+    dma = {}
+    for ahead in (1, 2, 4):
+        ms = timed(lambda: lib.moe_roof_dma_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), K, ahead, cus,
+                                                 ctypes.c_void_p(sink.data_ptr()), sp))
+        dma[ahead] = dma_bytes / (ms * 1e-3) / 1e9
+    # latency of a load that misses every cache: a chain of dependent loads in
+    # random order over the buffer's first 2 GiB, one entry per 128-byte line;
+    # streaming the other half afterwards evicts the chain from the caches
+    lines = 1 << 24
+    nxt = buf.view(torch.int32)[: lines * 32]
+    perm = torch.randperm(lines, device="cuda", generator=torch.Generator(device="cuda").manual_seed(7))
+    nxt[perm * 32] = (torch.roll(perm, -1) * 32).to(torch.int32)
+    del perm
+    half = buf[(lines * 128):]
+    lib.moe_roof_hbm_read(ctypes.c_void_p(half.data_ptr()), half.numel(), 2 * cus,
+                          ctypes.c_void_p(sink.data_ptr()), sp)
+    # each run continues the chain where the previous one stopped, so every
+    # run reads lines no run has touched since the eviction
+    steps, pos, ms = 20000, 0, []
+    for _ in range(4):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        moe._lib.check("roof", lib.moe_roof_hbm_latency(ctypes.c_void_p(nxt.data_ptr()), nxt.numel(), pos, steps,
+                                                        ctypes.c_void_p(sink.data_ptr()), sp))
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+        pos = int(sink[:1].view(torch.int32).item())
+    latency_ns = float(np.median(ms[1:])) * 1e6 / steps
+    del buf, sink, nxt, half
     torch.cuda.empty_cache()
+    per_cu = dma[1] * 1e9 / cus                     # bytes per second per CU, one block per wave in flight
     return {"fp8_mfma_tflops": flop / (ms_mfma * 1e-3) / 1e12,
             "hbm_read_gbs": (4 << 30) / (ms_read * 1e-3) / 1e9,
+            "hbm_dma_gbs": {str(a): v for a, v in dma.items()},
+            "hbm_latency_ns": latency_ns,
+            "lines_in_flight_per_cu": per_cu * latency_ns * 1e-9 / 128,
             "note": "moe_roof_fp8_mfma: 8 independent FP8 MFMA chains per wave, no memory traffic, "
                     f"{wg_mfma} workgroups x 4 waves; moe_roof_hbm_read: non-temporal 16-byte loads over "
-                    f"a 4 GiB buffer, a contiguous share per workgroup, {2 * cus} workgroups; median of "
-                    f"{reps} runs each"}
+                    f"a 4 GiB buffer, a contiguous share per workgroup, {2 * cus} workgroups; "
+                    f"moe_roof_dma_read: rows of {K} bytes, 8 waves per CU, each streaming 32 rows into its "
+                    "LDS ring with 1, 2 or 4 K blocks of 4 KB in flight; moe_roof_hbm_latency: "
+                    f"{steps} dependent loads in random order over 2 GiB (unloaded latency); "
+                    "lines_in_flight_per_cu: the DMA rate with one block in flight per wave, per CU, "
+                    "times that latency over 128 bytes (Little's law; a lower bound, since the latency "
+                    f"under load is higher); median of {reps} runs each"}
 
 
 def decode_leg(W, roofs, steps, warmup):
@@ -319,7 +362,10 @@ def main():
     roofs = None if args.no_roofs else measured_roofs()
     if roofs is not None:
         log(f"measured roofs: FP8 MFMA {roofs['fp8_mfma_tflops']:.0f} TFLOP/s, "
-            f"HBM read {roofs['hbm_read_gbs']:.0f} GB/s")
+            f"HBM read {roofs['hbm_read_gbs']:.0f} GB/s; weight-pattern direct loads "
+            + ", ".join(f"{v:.0f}" for v in roofs["hbm_dma_gbs"].values())
+            + f" GB/s at 1, 2, 4 blocks in flight; load latency {roofs['hbm_latency_ns']:.0f} ns; "
+            f"≥ {roofs['lines_in_flight_per_cu']:.0f} lines in flight per CU")
     decode = None
     if not args.no_decode and cfg.name != "decode_64":
         decode = decode_leg(W, roofs or {"hbm_read_gbs": float("nan")}, args.steps, args.warmup)

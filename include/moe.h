@@ -389,7 +389,7 @@ moe_status grouped_gemm_fp8_wgrad(const uint8_t* a_t, const float* a_ts, const u
                                   const float* b_ts, const int32_t* offsets, int n_groups,
                                   int total_rows, int M, int N, float* dw, void* stream);
 
-/* Measurement utilities (not steps of the layer): the two roofs the layer's
+/* Measurement utilities (not steps of the layer): the roofs the layer's
  * kernels are bound by, measured on the device, to read a kernel's rate
  * against beside the datasheet peaks (5.0 PFLOP/s dense FP8, 8 TB/s).
  *
@@ -402,10 +402,28 @@ moe_status grouped_gemm_fp8_wgrad(const uint8_t* a_t, const float* a_ts, const u
  *   bytes % 16 == 0) once with 16-byte loads from `workgroups` workgroups of
  *   256 threads; sink [workgroups * 256] uint32 out (an XOR of the words each
  *   thread read).  Use a buffer much larger than the 256 MB last-level cache.
- * Both: asynchronous on `stream`; the caller times them (HIP events). */
+ * moe_roof_dma_read — the expert GEMMs' weight-load pattern alone: buf
+ *   [rows, K] bytes (16-byte aligned, K a multiple of 128; the first
+ *   32 * floor(bytes / (32 K)) rows are read).  `workgroups` workgroups of 8
+ *   waves; each wave streams 32 rows K block by K block with direct
+ *   global->LDS loads of whole 128-byte lines into an LDS ring, `ahead`
+ *   (1, 2 or 4) blocks of 4 KB in flight per wave.  sink [workgroups * 512]
+ *   uint32 out (K blocks each thread's wave streamed).
+ * moe_roof_hbm_latency — one lane follows `steps` links of the chain in
+ *   next [n] uint32 (caller-built: next[i] is the index of the entry read
+ *   after entry i; an index >= n is clamped to n - 1) from entry `start`;
+ *   time / steps is the latency of a dependent load.  sink [1] uint32 out
+ *   (the last index).  Lay the chain over a buffer much larger than the
+ *   last-level cache, one entry per 128-byte line, in random order.
+ * All four: asynchronous on `stream`; the caller times them (HIP events).
+ * Errors: MOE_ERR_INVALID_ARG for sizes or pointers outside the ranges above. */
 moe_status moe_roof_fp8_mfma(int workgroups, int iters, float* sink, void* stream);
 moe_status moe_roof_hbm_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
                              void* stream);
+moe_status moe_roof_dma_read(const void* buf, size_t bytes, int K, int ahead, int workgroups, uint32_t* sink,
+                             void* stream);
+moe_status moe_roof_hbm_latency(const uint32_t* next, size_t n, uint32_t start, int steps, uint32_t* sink,
+                                void* stream);
 
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);

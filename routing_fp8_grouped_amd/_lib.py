@@ -46,6 +46,8 @@ SIGNATURES = {
     "moe_permute_noalloc": (I, [P, I, I, I, P, P, I, P, P, P, P, P, P]),
     "moe_roof_fp8_mfma": (I, [I, I, P, P]),
     "moe_roof_hbm_read": (I, [P, SZ, I, P, P]),
+    "moe_roof_dma_read": (I, [P, SZ, I, I, I, P, P]),
+    "moe_roof_hbm_latency": (I, [P, SZ, ctypes.c_uint32, I, P, P]),
     "grouped_gemm_fp8_swiglu": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P, P, P, P]),
     "grouped_gemm_fp8_up": (I, [P, P, I, P, P, I, I, I, I, P, P, P, P, P]),
     "grouped_gemm_fp8_down": (I, [P, P, P, I, I, I, I, P, P, P, P]),

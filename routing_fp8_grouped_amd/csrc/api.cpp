@@ -631,4 +631,30 @@ moe_status moe_roof_hbm_read(const void* buf, size_t bytes, int workgroups, uint
                     "moe_roof_hbm_read launch");
 }
 
+moe_status moe_roof_dma_read(const void* buf, size_t bytes, int K, int ahead, int workgroups, uint32_t* sink,
+                             void* stream) {
+  clear_error();
+  REQUIRE(workgroups >= 1 && workgroups <= (1 << 20), "workgroups=%d must be in [1, 2^20]", workgroups);
+  REQUIRE(K >= 128 && K % 128 == 0 && K <= (1 << 20), "K=%d must be a multiple of 128 in [128, 2^20]", K);
+  REQUIRE(ahead == 1 || ahead == 2 || ahead == 4, "ahead=%d must be 1, 2 or 4", ahead);
+  REQUIRE(bytes / ((size_t)K * 32) >= 1, "bytes=%zu holds no 32 rows of K=%d bytes", bytes, K);
+  REQUIRE(bytes / ((size_t)K * 32) < (size_t)(1u << 31) - 8, "bytes=%zu: too many 32-row slabs", bytes);
+  REQUIRE_PTR(buf);
+  REQUIRE_PTR4(sink);
+  return hip_status(moe::launch_roof_dma(buf, bytes, K, ahead, workgroups, sink, static_cast<hipStream_t>(stream)),
+                    "moe_roof_dma_read launch");
+}
+
+moe_status moe_roof_hbm_latency(const uint32_t* next, size_t n, uint32_t start, int steps, uint32_t* sink,
+                                void* stream) {
+  clear_error();
+  REQUIRE(n >= 1 && n <= 0xFFFFFFFFull, "n=%zu must be in [1, 2^32 - 1]", n);
+  REQUIRE(start < n, "start=%u must be < n=%zu", start, n);
+  REQUIRE(steps >= 1, "steps=%d must be >= 1", steps);
+  REQUIRE_PTR4(next);
+  REQUIRE_PTR4(sink);
+  return hip_status(moe::launch_roof_chase(next, n, start, steps, sink, static_cast<hipStream_t>(stream)),
+                    "moe_roof_hbm_latency launch");
+}
+
 }  // extern "C"

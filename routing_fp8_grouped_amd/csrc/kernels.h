@@ -85,6 +85,10 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
 
 // Measured roofs (roofs.hip): FP8 MFMA issue rate and HBM read streaming.
 hipError_t launch_roof_mfma(int workgroups, int iters, float* sink, hipStream_t stream);
+hipError_t launch_roof_dma(const void* buf, size_t bytes, int K, int ahead, int workgroups, uint32_t* sink,
+                           hipStream_t stream);
+hipError_t launch_roof_chase(const uint32_t* next, size_t n, uint32_t start, int steps, uint32_t* sink,
+                             hipStream_t stream);
 hipError_t launch_roof_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
                             hipStream_t stream);
 

@@ -37,6 +37,7 @@ def test_exports_every_declared_symbol(lib):
                              "moe_wgrad_columns", "moe_regroup_128x1",
                              "moe_swiglu_backward", "grouped_gemm_fp8_wgrad",
                              "moe_roof_fp8_mfma", "moe_roof_hbm_read",
+                             "moe_roof_dma_read", "moe_roof_hbm_latency",
                              "moe_status_string", "moe_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -256,3 +257,13 @@ def test_roof_validation(lib):
     assert lib.moe_roof_fp8_mfma(4, 10, None, None) == 1 and "sink" in last(lib)
     assert lib.moe_roof_hbm_read(A, 24, 4, A, None) == 1 and "bytes" in last(lib)
     assert lib.moe_roof_hbm_read(MIS, 32, 4, A, None) == 1 and "buf" in last(lib)
+    big = 32 * 7168
+    assert lib.moe_roof_dma_read(A, big, 7168, 3, 4, A, None) == 1 and "ahead" in last(lib)
+    assert lib.moe_roof_dma_read(A, big, 7000, 1, 4, A, None) == 1 and "K=" in last(lib)
+    assert lib.moe_roof_dma_read(A, big - 1, 7168, 1, 4, A, None) == 1 and "bytes" in last(lib)
+    assert lib.moe_roof_dma_read(A, big, 7168, 1, 0, A, None) == 1 and "workgroups" in last(lib)
+    assert lib.moe_roof_dma_read(None, big, 7168, 1, 4, A, None) == 1 and "buf" in last(lib)
+    assert lib.moe_roof_hbm_latency(A, 0, 0, 10, A, None) == 1 and "n=" in last(lib)
+    assert lib.moe_roof_hbm_latency(A, 64, 64, 10, A, None) == 1 and "start" in last(lib)
+    assert lib.moe_roof_hbm_latency(A, 64, 0, 0, A, None) == 1 and "steps" in last(lib)
+    assert lib.moe_roof_hbm_latency(MIS4, 64, 0, 10, A, None) == 1 and "next" in last(lib)
