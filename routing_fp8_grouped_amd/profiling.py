@@ -3,10 +3,15 @@
     python -m routing_fp8_grouped_amd.profiling stats DIR --command CMD
     python -m routing_fp8_grouped_amd.profiling traffic FETCH_DIR WRITE_DIR \\
         --workload NAME --command-fetch CMD --command-write CMD
+    python -m routing_fp8_grouped_amd.profiling counters DIR [DIR ...] \\
+        --kernel FRAGMENT [--kernel ...] --command CMD [--command ...]
 
 ``stats`` condenses ``rocprofv3 --kernel-trace --stats --output-format csv``
 (the ``*kernel_stats.csv`` file) into a short table of per-kernel call
 counts and durations.
+
+``counters`` averages every counter of one or more ``rocprofv3 --pmc`` runs
+per dispatch of the kernels whose names contain the given fragments.
 
 ``traffic`` turns two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
 runs of ``bench.py`` into HBM bytes per launch of the first expert GEMM (the
@@ -60,6 +65,8 @@ KERNELS = {
     "bias_update_kernel": "moe_bias_update",
     "roof_mfma_kernel": "moe_roof_fp8_mfma",
     "roof_read_kernel": "moe_roof_hbm_read",
+    "roof_dma_kernel": "moe_roof_dma_read",
+    "roof_chase_kernel": "moe_roof_hbm_latency",
 }
 GIB_KIB = float(1 << 20)
 
@@ -120,6 +127,26 @@ def per_dispatch(d, counter):
     return {k: (names[k], v) for k, v in vals.items()}
 
 
+def counters(dirs, fragments):
+    """{kernel label: {counter: (mean per dispatch, dispatches)}} over the
+    --pmc runs in ``dirs``, for kernels whose names contain a fragment."""
+    per = collections.defaultdict(float)
+    names = {}
+    for d in dirs:
+        for path in _find(d, "counter_collection.csv"):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if not any(fr in r["Kernel_Name"] for fr in fragments):
+                        continue
+                    per[(path, r["Dispatch_Id"], r["Counter_Name"])] += float(r["Counter_Value"])
+                    names[(path, r["Dispatch_Id"])] = r["Kernel_Name"]
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (path, disp, counter), v in per.items():
+        name = names[(path, disp)]
+        agg[_short(name) or name[:60]][counter].append(v)
+    return {k: {c: (sum(v) / len(v), len(v)) for c, v in cs.items()} for k, cs in agg.items()}
+
+
 def traffic(fetch_dir, write_dir, kernel_frag=TILED):
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -146,10 +173,23 @@ def main(argv=None):
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--kernel", default=TILED, choices=sorted(KERNEL_SOURCES))
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--command", action="append", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(f"rocprofv3 kernel statistics\ncommand: {a.command}\n")
         print("\n".join(stats_table(a.dir)))
+        return
+    if a.cmd == "counters":
+        print("rocprofv3 hardware counters, mean per dispatch")
+        for cmd in a.command:
+            print(f"command: {cmd}")
+        for k, cs in sorted(counters(a.dirs, a.kernel).items()):
+            print(f"\n{k}")
+            for cname, (v, n) in sorted(cs.items()):
+                print(f"    {cname:<32} {v:12.5g}   ({n} dispatches)")
         return
     r = traffic(a.fetch_dir, a.write_dir, a.kernel)
     f, w = r["FETCH_SIZE"], r["WRITE_SIZE"]
