@@ -40,7 +40,7 @@ class MoEConfig:
 
 V3 = dict(d=7168, E=256, G=8, M=4, k=8, f=2048)
 
-# The skew strength is fixed offline by oracle/calibrate_skew.py (bisection so
+# The skew strength is fixed offline by tests/calibrate_zipf_skew.py (bisection so
 # that the busiest routed expert receives about 4000 of the 16384*8 assignments).
 ZIPF_BETA = 2.885
 

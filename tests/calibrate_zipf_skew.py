@@ -1,7 +1,8 @@
 """Pick the strength of the rank-1 Zipf component of the skewed 16384-token workload.
 
-Test infrastructure (see ``oracle/__init__.py``): run once by hand, prints the
-value stored as ``ZIPF_BETA`` in ``routing_fp8_grouped_amd/configs.py``.
+Test infrastructure, kept beside the tests rather than in ``oracle/`` because
+it reads the package's input recipe: run once by hand, it prints the value
+stored as ``ZIPF_BETA`` in ``routing_fp8_grouped_amd/configs.py``.
 
 The skewed workload adds beta * a (x) v to the router centroids, with
 a_e = r_e^-1.1 - mean(r^-1.1) over a seeded rank permutation r, so the
@@ -11,7 +12,7 @@ slots), so beta is chosen by bisection such that the busiest routed expert gets
 about 4000 of the 16384 * 8 slots and the least busy get close to none.  Routing
 is the oracle's.
 
-    python -m oracle.calibrate_skew
+    python -m tests.calibrate_zipf_skew
 """
 
 import dataclasses
@@ -19,7 +20,7 @@ import sys
 
 import numpy as np
 
-from .route import route
+from oracle.route import route
 
 
 def counts_for(cfg, beta, x, inputs):
