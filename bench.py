@@ -285,6 +285,21 @@ def decode_leg(W, roofs, steps, warmup):
         layer.forward(x, wg, b, W)
     torch.cuda.synchronize()
     ms, st = timed_steps(layer, x, wg, b, W, steps)
+    # cold: each step after a 1 GiB write has evicted the 256 MB last-level
+    # cache (the weights are 36x that, so cold and warm should agree)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    cold = []
+    for i in range(max(3, steps // 2)):
+        flush.fill_(i & 0xFF)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        layer.forward(x, wg, b, W)
+        e.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(e))
+    del flush
+    cold_ms = float(np.median(cold))
     counts = np.bincount(layer.idx.cpu().numpy().reshape(-1), minlength=cfg.E)
     touched = int((counts > 0).sum()) + 1
     d, f = cfg.d, cfg.f
@@ -295,13 +310,14 @@ def decode_leg(W, roofs, steps, warmup):
     up_s = st["gemm_up"] * 1e-3
     layer_gbs = layer_bytes / (ms * 1e-3) / 1e9
     up_gbs = up_bytes / up_s / 1e9
-    log(f"decode_64: {ms:.3f} ms/step, {touched} experts touched, layer {layer_gbs:.0f} GB/s; stages " +
-        ", ".join(f"{k} {v:.3f}" for k, v in st.items()))
+    log(f"decode_64: {ms:.3f} ms/step (cold {cold_ms:.3f}), {touched} experts touched, layer "
+        f"{layer_gbs:.0f} GB/s; stages " + ", ".join(f"{k} {v:.3f}" for k, v in st.items()))
     return {
         "workload": cfg.name, "tokens": cfg.T, "ms_per_step": ms, "tokens_per_s": cfg.T / (ms * 1e-3),
         "stages_ms": st, "experts_touched": touched, "algorithmic_bytes": layer_bytes,
         "hbm_gbs": layer_gbs, "hbm_frac_of_peak": layer_gbs / HBM_PEAK_GBS,
         "hbm_frac_of_measured": layer_gbs / roofs["hbm_read_gbs"],
+        "cold_ms_per_step": cold_ms, "cold_hbm_gbs": layer_bytes / (cold_ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": up_gbs / HBM_PEAK_GBS, "measured_peak": roofs["hbm_read_gbs"],
                      "frac_of_measured": up_gbs / roofs["hbm_read_gbs"],
@@ -310,7 +326,8 @@ def decode_leg(W, roofs, steps, warmup):
                      "traffic": read_traffic(cfg.name, profiling.STREAMING)},
         "note": "algorithmic bytes: each touched expert's W1, W3, W2 codes and scales once, the "
                 "router weights, the token rows in and the output out; the same resident weights "
-                "as the headline workload (same shapes and distribution)",
+                "as the headline workload (same shapes and distribution); cold: the median of single "
+                "steps each after a 1 GiB write that evicts the last-level cache",
     }
 
 
