@@ -7,8 +7,9 @@
 // One workgroup (8 waves) routes 64 tokens against all (<= 256) experts:
 //   1. logits: BF16 MFMA 16x16x32, FP32 partial sums over each 128-wide chunk
 //      of d, chunks summed in FP64 registers.  Token rows and centroid rows
-//      stream through a two-stage LDS ring (64 elements of d per stage) by
-//      direct global->LDS loads; wave w owns experts 32 w .. 32 w + 31.  The
+//      stream through a three-stage LDS ring (64 elements of d per stage, so
+//      every direct global->LDS load fetches whole 128-byte lines; the kernel
+//      is bound by its request rate); wave w owns experts 32 w .. 32 w + 31.  The
 //      FP64 logits are stored to LDS rounded to FP32 (relative 6e-8: the
 //      biased scores move by < 1e-7, far inside the 1e-6 near-tie band).
 //   2. selection, one token per wave at a time, in FP64: per-group sum of the
@@ -25,11 +26,11 @@ namespace moe {
 constexpr int RT_TOK = 64;
 constexpr int RT_EXP = 256;
 constexpr int RT_THREADS = 512;
-constexpr int RT_KS = 32;                              // d elements per ring stage
-constexpr int RT_ROWB = RT_KS * 2;                     // 64-byte rows
-constexpr int RT_A = RT_TOK * RT_ROWB;                 // token rows of a stage, 4 KB
-constexpr int RT_STG = (RT_TOK + RT_EXP) * RT_ROWB;    // 20 KB
-constexpr int RT_NST = 6;                              // ring depth
+constexpr int RT_KS = 64;                              // d elements per ring stage
+constexpr int RT_ROWB = RT_KS * 2;                     // 128-byte rows: whole cache lines
+constexpr int RT_A = RT_TOK * RT_ROWB;                 // token rows of a stage, 8 KB
+constexpr int RT_STG = (RT_TOK + RT_EXP) * RT_ROWB;    // 40 KB
+constexpr int RT_NST = 3;                              // ring depth
 constexpr int RT_LSTRIDE = RT_EXP + 1;                 // FP32 logit table row stride
 constexpr int RT_MAXG = 64;
 
@@ -39,9 +40,10 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// LDS layout of a 64-byte row r: its 16-byte chunk c sits at c ^ ((r >> 2) & 3),
-// so a fragment read (16 lanes on rows r0..r0+15, one chunk) covers all banks.
-__device__ __forceinline__ int rt_off(int r, int c) { return r * RT_ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
+// LDS layout of a 128-byte row r: its 16-byte chunk c sits at c ^ op_swz(r),
+// the operand layout of the expert GEMMs (a fragment read, 16 lanes on rows
+// r0..r0+15 at one chunk, spreads over the banks).
+__device__ __forceinline__ int rt_off(int r, int c) { return r * RT_ROWB + ((c ^ op_swz(r)) << 4); }
 
 __device__ __forceinline__ v8bf rt_frag(const unsigned char* T, int r, int c) {
   return *reinterpret_cast<const v8bf*>(T + rt_off(r, c));
@@ -336,32 +338,32 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(const uint16_t* __res
   if (threadIdx.x < RT_EXP) sbias[threadIdx.x] = (bias && (int)threadIdx.x < E) ? bias[threadIdx.x] : 0.0f;
 
   // ---- logits ----
-  // Direct loads: an instruction writes 1 KB = 16 rows of 64 bytes; lane l
-  // fills row 16 i + l / 4, physical chunk l % 4 with the logical chunk
-  // (l % 4) ^ ((row >> 2) & 3).  Wave w loads expert rows 32 w .. 32 w + 31 (its
-  // own experts) and, for w < 4, token rows 16 w .. 16 w + 15; rows past T or E
-  // repeat the last valid row (their results are never used).
-  const int pc = lane & 3;
-  uint32_t a_off = 0, b_off[2];
-  if (wave < 4) {
-    const int r = wave * 16 + (lane >> 2);
+  // Direct loads of whole 128-byte lines: an instruction writes 1 KB = 8 rows;
+  // lane l fills row 8 i + l / 8, physical chunk l % 8 with the logical chunk
+  // (l % 8) ^ op_swz(row).  Wave w loads expert rows 32 w .. 32 w + 31 (its own
+  // experts, 4 loads) and token rows 8 w .. 8 w + 7 (1 load); rows past T or
+  // E repeat the last valid row (their results are never used).
+  const int pc = lane & 7;
+  uint32_t a_off, b_off[4];
+  {
+    const int r = wave * 8 + (lane >> 3);
     const int t = min(t0 + r, T - 1);
-    a_off = (uint32_t)t * (uint32_t)d * 2u + (uint32_t)((pc ^ ((r >> 2) & 3)) * 16);
+    a_off = (uint32_t)t * (uint32_t)d * 2u + (uint32_t)((pc ^ op_swz(r)) * 16);
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = wave * 32 + i * 16 + (lane >> 2);
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 32 + i * 8 + (lane >> 3);
     const int e = min(r, E - 1);
-    b_off[i] = (uint32_t)e * (uint32_t)d * 2u + (uint32_t)((pc ^ ((r >> 2) & 3)) * 16);
+    b_off[i] = (uint32_t)e * (uint32_t)d * 2u + (uint32_t)((pc ^ op_swz(r)) * 16);
   }
   const uint32_t ring0 = lds_addr(ring);
 #define RT_ISSUE(ks_)                                                                        \
   do {                                                                                       \
     const int ks__ = (ks_);                                                                  \
     const uint32_t base__ = ring0 + (ks__ % RT_NST) * RT_STG;                                \
-    if (wave < 4) dma16(x + (size_t)ks__ * RT_KS, a_off, base__ + wave * 1024);              \
-    dma16(wg + (size_t)ks__ * RT_KS, b_off[0], base__ + RT_A + (wave * 2) * 1024);           \
-    dma16(wg + (size_t)ks__ * RT_KS, b_off[1], base__ + RT_A + (wave * 2 + 1) * 1024);       \
+    dma16(x + (size_t)ks__ * RT_KS, a_off, base__ + wave * 1024);                            \
+    _Pragma("unroll") for (int i__ = 0; i__ < 4; ++i__)                                      \
+      dma16(wg + (size_t)ks__ * RT_KS, b_off[i__], base__ + RT_A + (wave * 4 + i__) * 1024); \
   } while (0)
 
   double acc64[4][2][4];
@@ -375,13 +377,14 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(const uint16_t* __res
       for (int i = 0; i < 4; ++i) acc64[mt][nt][i] = 0.0;
     }
 
-  // stages 0 .. RT_NST-2 in flight (d >= 128, so n_ks >= 4)
+  // stages 0 .. RT_NST-2 in flight (d >= 128, so n_ks >= 2)
   for (int ks = 0; ks < RT_NST - 1 && ks < n_ks; ++ks) RT_ISSUE(ks);
   for (int ks = 0; ks < n_ks; ++ks) {
-    // stage ks has landed once at most the younger stages are outstanding
+    // stage ks has landed once at most the younger stages (5 loads each) are
+    // outstanding
     const int younger = min(RT_NST - 2, n_ks - 1 - ks);
     if (younger >= RT_NST - 2) {
-      if (wave < 4) rt_wait_vmcnt<3 * (RT_NST - 2)>(); else rt_wait_vmcnt<2 * (RT_NST - 2)>();
+      rt_wait_vmcnt<5 * (RT_NST - 2)>();
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the tail of the loop
     }
@@ -389,16 +392,19 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(const uint16_t* __res
     if (ks + RT_NST - 1 < n_ks) RT_ISSUE(ks + RT_NST - 1);
     const unsigned char* A = ring + (ks % RT_NST) * RT_STG;
     const unsigned char* B = A + RT_A;
-    v8bf af[4], bf[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) af[mt] = rt_frag(A, mt * 16 + r16, g16);
+    for (int kk = 0; kk < 2; ++kk) {   // two 32-wide halves of the stage's 64 elements of d
+      v8bf af[4], bf[2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) bf[nt] = rt_frag(B, wave * 32 + nt * 16 + r16, g16);
+      for (int mt = 0; mt < 4; ++mt) af[mt] = rt_frag(A, mt * 16 + r16, kk * 4 + g16);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt) bf[nt] = rt_frag(B, wave * 32 + nt * 16 + r16, kk * 4 + g16);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_bf16_16x16x32(af[mt], bf[nt], acc[mt][nt]);
-    if ((ks & 3) == 3) {   // a 128-wide chunk of d is complete: promote to FP64
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_bf16_16x16x32(af[mt], bf[nt], acc[mt][nt]);
+    }
+    if ((ks & 1) == 1) {   // a 128-wide chunk of d is complete: promote to FP64
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
