@@ -13,7 +13,12 @@ The default workload is the V3 layer at 16384 tokens with near-uniform expert
 load, the headline case for the grouped FP8 GEMM.  ``roofline`` reports the
 dominant kernel (the first expert GEMM, 2/3 of the FLOPs) against the MI355X
 dense FP8 MFMA peak, timed with HIP events on the stream it runs on;
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload,
+and (``tiny_one_core``) on the whole tiny workload with one BLAS thread.
+``measured_roofs`` measures the FP8 MFMA rate, the HBM read rate, the
+direct-load stream rate and the unloaded miss latency on this GPU; ``decode``
+times the 64-token workload on the same resident weights (HBM-bound) and
+``tiny`` the 256-token tiny workload (launch-bound).
 ``e8m0_variant`` times the same workload once more with power-of-two scales on
 the hardware block-scaled MFMA (weights requantised with that rule, outside
 the timed region); the headline ``value`` is the FP32-scale method.
@@ -115,13 +120,63 @@ def cpu_baseline(cfg, n_tokens):
     t0 = time.perf_counter()
     olayer.moe_layer_tokens(x, wg, b, lambda e: q[e], cfg.G, cfg.M, cfg.k, cfg.route_scale)
     dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "affinity_cores": affinity, "blas_threads": int(blas),
+    out = {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "affinity_cores": affinity, "blas_threads": int(blas),
             "sample": f"first {n_tokens} token(s) of the {cfg.name} workload, whole layer "
                       f"({len(need)} experts incl. shared), {dt:.1f} s; expert weights "
                       "quantised by the oracle beforehand (untimed, as on the GPU); cores = "
                       "min(sched_getaffinity cores, BLAS threads): the oracle's products run "
                       "on the BLAS threads, its loops on one Python thread"}
+    out["tiny_one_core"] = oracle_tiny_one_core()
+    return out
+
+
+def oracle_tiny_one_core(min_seconds=2.0):
+    """The oracle on all 256 tokens of the tiny configuration with its BLAS
+    limited to one thread: the median of repeated passes (about two seconds of
+    work), expert weights quantised beforehand (untimed)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import layer as olayer
+    cfg = configs.get("tiny")
+    x = inputs.activations(cfg).float().numpy()
+    wg = inputs.router_weights(cfg).float().numpy()
+    b = inputs.selection_bias(cfg).numpy()
+    q = {}
+    for e in range(cfg.E + 1):
+        w13, w2 = inputs.expert_weights(cfg, e, "cuda")     # the GPU leg's values
+        q[e] = olayer.quantize_expert(w13.float().cpu().numpy(), w2.float().cpu().numpy())
+    times = []
+    with threadpool_limits(1):
+        while sum(times) < min_seconds or len(times) < 3:
+            t0 = time.perf_counter()
+            olayer.moe_layer_tokens(x, wg, b, lambda e: q[e], cfg.G, cfg.M, cfg.k, cfg.route_scale)
+            times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {"value": cfg.T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {cfg.T} tokens of the tiny workload (d {cfg.d}, {cfg.E}+1 experts, k {cfg.k}), "
+                      f"BLAS limited to one thread; median of {len(times)} passes, {dt * 1e3:.1f} ms each"}
+
+
+def tiny_leg(steps, warmup):
+    """The tiny configuration (256 tokens, d 256, 16 routed experts): a layer
+    whose kernels are each far below a microsecond of work, so its time is the
+    launches' (eager, and replayed from a HIP graph)."""
+    cfg = configs.get("tiny")
+    x, wg, b = (t.cuda() for t in inputs.host_inputs(cfg))
+    W = build_weights(cfg)
+    layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.f, cfg.route_scale)
+    for _ in range(warmup):
+        layer.forward(x, wg, b, W)
+    torch.cuda.synchronize()
+    ms, st = timed_steps(layer, x, wg, b, W, steps)
+    graph_ms = timed_graph(layer, x, wg, b, W, steps)
+    log(f"tiny: {ms:.3f} ms/step eager, {graph_ms:.3f} ms/step from a graph; stages "
+        + ", ".join(f"{k} {v:.3f}" for k, v in st.items()))
+    return {"workload": cfg.name, "tokens": cfg.T, "ms_per_step": ms, "tokens_per_s": cfg.T / (ms * 1e-3),
+            "graph_ms_per_step": graph_ms, "graph_tokens_per_s": cfg.T / (graph_ms * 1e-3),
+            "stages_ms": st,
+            "note": "launch-bound: each of the six stages is one to a few small kernels; the graph "
+                    "replay removes the host's launch gaps"}
 
 
 def timed_steps(layer, x, wg, b, W, steps):
@@ -346,6 +401,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the timing of the backward")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode_64 leg")
     ap.add_argument("--no-roofs", action="store_true", help="skip the measured roofs")
+    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny-configuration leg")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -465,6 +521,8 @@ def main():
         result["measured_roofs"] = roofs
     if decode is not None:
         result["decode"] = decode
+    if not args.no_tiny and cfg.name != "tiny":
+        result["tiny"] = tiny_leg(args.steps, args.warmup)
     if not args.no_backward:
         Wt = W.transposed()
         layer.forward(x, wg, b, W, train=True)
