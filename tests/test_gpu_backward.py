@@ -481,6 +481,15 @@ def test_v3_backward_sampled():
     dx, dw13, dw2, dgate = L.backward(dout, Wt)
     torch.cuda.synchronize()
     log("  forward + backward done on the GPU")
+    # the backward again on the same cache gives the same bytes (the gradients
+    # are written, never accumulated with atomics)
+    first = [t.clone() for t in (dx, dw13, dw2, dgate)]
+    again = L.backward(dout, Wt)
+    torch.cuda.synchronize()
+    for nm, a, c in zip(("dx", "dw13", "dw2", "dgate"), first, again):
+        assert torch.equal(a, c), nm
+    del first
+    log("  second backward identical")
     pos, off = to_np(L.pos), to_np(L.offsets)
     rt = to_np(L.row_token)
     rng = np.random.default_rng(8)

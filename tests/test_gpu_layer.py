@@ -164,6 +164,13 @@ def test_v3_workload(name):
     log("  weights quantised on the GPU")
     L = run_layer(cfg, x, wg, b, W)
     log("  layer done on the GPU")
+    # a second run of the same step in a fresh layer gives the same bytes in
+    # every buffer (no order-dependent atomics; integer counters only)
+    L2 = run_layer(cfg, x, wg, b, W)
+    for nm in ("idx", "w", "xq", "xs", "offsets", "pos", "row_token", "h", "hs", "y", "out"):
+        assert torch.equal(getattr(L, nm), getattr(L2, nm)), nm
+    del L2
+    log("  second run identical in every buffer")
     xn = x.float().numpy()
     r = oroute.route(xn, wg.float().numpy(), b.numpy(), cfg.G, cfg.M, cfg.k, cfg.route_scale)
     gi = to_np(L.idx)
