@@ -8,10 +8,20 @@ within the bound of test_combine_parity.  The fixed parameter lists of
 test_gpu_kernels.py cover chosen shapes; these cover the space between them
 (group sizes from 1 to 64 experts, 1 to 16 experts per token, ragged T).
 
+A second sweep runs the whole layer (router, 1x128 quantisation, permutation,
+both expert GEMMs, combine) on seeded draws of T in [1, 300], E in {8, 16,
+32} with G dividing E, and d, f in {128, 256, 384}: the small draws take the
+weight-streaming GEMM, the larger ones the tiled GEMM.  Each is held to the
+bar of the tiny layer in test_gpu_layer.py on every token: routing and
+quantisation bit for bit outside near ties, the permutation's properties,
+the stage-fed output within 5e-3 per row, H codes equal where unambiguous,
+and the independent chain within its counted allowance.
+
 Router: "DeepSeek-V3" summary page, section 1 (DeepSeekMoE, node-limited
 routing) and section 2 (routing-only bias); dispatch and combine: the book's
 chapter 15 "What dispatch must do", chapter 7 "Selecting and combining
-experts".
+experts"; the expert GEMMs: summary page section 6, the book's chapter 16
+"Periodic high-precision promotion".
 """
 
 import numpy as np
@@ -19,11 +29,16 @@ import pytest
 import torch
 
 import routing_fp8_grouped_amd as moe
+from routing_fp8_grouped_amd import configs, inputs
 from oracle import route as oroute, permute as operm, layer as olayer
-from tests.gpu_util import DEV, log, to_np
+from tests.gpu_util import (DEV, log, to_np, rel_l2_rows, device_weights, OracleExperts, run_layer,
+                            layer_allowance, rows_within, check_h_codes, chain_report,
+                            stage_fed_tokens)
 
 pytestmark = pytest.mark.gpu
 N_CASES = 24
+N_LAYERS = 16
+TOL = 5e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -104,3 +119,58 @@ def test_dispatch_chain_random(seed):
     assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 16 * 2.0 ** -24 * terms)
     log(f"  near-tie tokens: {int((~ok).sum())} of {T}; groups used max "
         f"{max(len(set((gi[t] // per).tolist())) for t in range(T))} of {M}")
+
+
+def draw_layer(seed):
+    """A whole-layer configuration: T in [1, 300], E in {8, 16, 32}, G | E,
+    M <= G, k = M * n <= min(M * E / G, 16), d and f in {128, 256, 384}."""
+    r = np.random.default_rng(9000 + seed)
+    E = int(r.choice([8, 16, 32]))
+    G = int(r.choice([g for g in (1, 2, 4, 8) if E % g == 0]))
+    per = E // G
+    M = int(r.integers(1, G + 1))
+    n_top = int(r.integers(1, min(per, 16 // M) + 1))
+    T = int(r.integers(1, 301))
+    d = int(r.choice([128, 256, 384]))
+    f = int(r.choice([128, 256, 384]))
+    rho = float(r.choice([1.0, 2.5]))
+    return configs.MoEConfig(f"fuzz{seed}", T=T, d=d, E=E, G=G, M=M, k=M * n_top, f=f,
+                             route_scale=rho, bias="zero" if seed % 4 == 0 else "uniform",
+                             seed=31000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(N_LAYERS))
+def test_layer_random(seed):
+    cfg = draw_layer(seed)
+    small = cfg.rows <= 16 * (cfg.E + 1)
+    log(f"layer fuzz seed={seed}: T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} G={cfg.G} M={cfg.M} "
+        f"k={cfg.k} rho={cfg.route_scale} ({'weight-streaming' if small else 'tiled'} GEMM)")
+    x, wg, b = inputs.host_inputs(cfg)
+    bf16 = {}
+    W = device_weights(cfg, bf16)
+    L = run_layer(cfg, x, wg, b, W)
+    oe = OracleExperts(cfg, bf16)
+    oe.prepare(range(cfg.E + 1))
+    ref = olayer.moe_layer(x.float().numpy(), wg.float().numpy(), b.numpy(), oe, cfg.G, cfg.M,
+                           cfg.k, cfg.route_scale)
+    r = ref["route"]
+    ok = ~r["near_tie"]
+    gi = to_np(L.idx)
+    assert np.array_equal(gi[ok], r["idx"][ok])
+    assert np.allclose(to_np(L.w)[ok], r["w"][ok], rtol=2e-6, atol=1e-7)
+    assert np.array_equal(to_np(L.xq), ref["xq"]) and np.array_equal(to_np(L.xs), ref["xs"])
+    same_route = np.array_equal(gi, r["idx"])
+    if same_route:
+        assert np.array_equal(to_np(L.offsets), ref["offsets"])
+        assert np.array_equal(to_np(L.pos), ref["pos"])
+        assert np.array_equal(to_np(L.row_token)[:cfg.T * cfg.k], ref["row_token"])
+    # stage-fed: the GPU's routing and H through the oracle's down GEMM and combine
+    sf = stage_fed_tokens(L, np.arange(cfg.T), oe, cfg.E)
+    err_sf = rel_l2_rows(to_np(L.out), sf)
+    assert np.all(err_sf <= TOL), err_sf.max()
+    allow, amb, sp = layer_allowance(ref, oe, cfg.T, cfg.k, cfg.E)
+    n_diff = check_h_codes(to_np(L.h), ref["hq"], amb, sp) if same_route else -1
+    okr, err, _ = rows_within(to_np(L.out)[ok], ref["out"][ok], allow[ok], TOL)
+    log(f"  near ties {int((~ok).sum())}; stage-fed rel-L2 max {err_sf.max():.2e}; h codes "
+        f"{int(amb.sum())} ambiguous, {n_diff} differ; " + chain_report(err, rows_within.allow_rel, TOL))
+    assert np.all(okr)
