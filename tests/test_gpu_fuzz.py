@@ -139,20 +139,25 @@ def draw_layer(seed):
                              seed=31000 + seed)
 
 
+def run_random_layer(cfg, rule):
+    small = cfg.rows <= 16 * (cfg.E + 1)
+    log(f"layer fuzz {cfg.name} ({rule} scales): T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} G={cfg.G} "
+        f"M={cfg.M} k={cfg.k} rho={cfg.route_scale} ({'weight-streaming' if small else 'tiled'} GEMM)")
+    x, wg, b = inputs.host_inputs(cfg)
+    bf16 = {}
+    W = device_weights(cfg, bf16, pow2=rule == "pow2")
+    L = run_layer(cfg, x, wg, b, W, scales=rule)
+    oe = OracleExperts(cfg, bf16, rule=rule)
+    oe.prepare(range(cfg.E + 1))
+    ref = olayer.moe_layer(x.float().numpy(), wg.float().numpy(), b.numpy(), oe, cfg.G, cfg.M,
+                           cfg.k, cfg.route_scale, rule=rule)
+    return L, ref, oe
+
+
 @pytest.mark.parametrize("seed", range(N_LAYERS))
 def test_layer_random(seed):
     cfg = draw_layer(seed)
-    small = cfg.rows <= 16 * (cfg.E + 1)
-    log(f"layer fuzz seed={seed}: T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} G={cfg.G} M={cfg.M} "
-        f"k={cfg.k} rho={cfg.route_scale} ({'weight-streaming' if small else 'tiled'} GEMM)")
-    x, wg, b = inputs.host_inputs(cfg)
-    bf16 = {}
-    W = device_weights(cfg, bf16)
-    L = run_layer(cfg, x, wg, b, W)
-    oe = OracleExperts(cfg, bf16)
-    oe.prepare(range(cfg.E + 1))
-    ref = olayer.moe_layer(x.float().numpy(), wg.float().numpy(), b.numpy(), oe, cfg.G, cfg.M,
-                           cfg.k, cfg.route_scale)
+    L, ref, oe = run_random_layer(cfg, "fp32")
     r = ref["route"]
     ok = ~r["near_tie"]
     gi = to_np(L.idx)
@@ -173,4 +178,26 @@ def test_layer_random(seed):
     okr, err, _ = rows_within(to_np(L.out)[ok], ref["out"][ok], allow[ok], TOL)
     log(f"  near ties {int((~ok).sum())}; stage-fed rel-L2 max {err_sf.max():.2e}; h codes "
         f"{int(amb.sum())} ambiguous, {n_diff} differ; " + chain_report(err, rows_within.allow_rel, TOL))
+    assert np.all(okr)
+
+
+@pytest.mark.parametrize("seed", range(N_LAYERS, N_LAYERS + 8))
+def test_layer_random_pow2(seed):
+    """The power-of-two scale variant (hardware block-scaled MFMA) on further
+    draws, against the oracle run with the power-of-two rule: routing and
+    quantisation bit for bit, the stage-fed output within 5e-3 per row, the
+    independent chain within its counted allowance."""
+    cfg = draw_layer(seed)
+    L, ref, oe = run_random_layer(cfg, "pow2")
+    r = ref["route"]
+    ok = ~r["near_tie"]
+    assert np.array_equal(to_np(L.idx)[ok], r["idx"][ok])
+    assert np.array_equal(to_np(L.xq), ref["xq"]) and np.array_equal(to_np(L.xs), ref["xs"])
+    sf = stage_fed_tokens(L, np.arange(cfg.T), oe, cfg.E)
+    err_sf = rel_l2_rows(to_np(L.out), sf)
+    assert np.all(err_sf <= TOL), err_sf.max()
+    allow, _, _ = layer_allowance(ref, oe, cfg.T, cfg.k, cfg.E, rule="pow2")
+    okr, err, _ = rows_within(to_np(L.out)[ok], ref["out"][ok], allow[ok], TOL)
+    log(f"  near ties {int((~ok).sum())}; stage-fed rel-L2 max {err_sf.max():.2e}; "
+        + chain_report(err, rows_within.allow_rel, TOL))
     assert np.all(okr)
