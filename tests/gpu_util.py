@@ -91,6 +91,24 @@ def host_inputs(cfg):
     return x, wg, b
 
 
+def random_layer_config(seed):
+    """A whole-layer configuration: T in [1, 300], E in {8, 16, 32}, G | E,
+    M <= G, k = M * n <= min(M * E / G, 16), d and f in {128, 256, 384}."""
+    r = np.random.default_rng(9000 + seed)
+    E = int(r.choice([8, 16, 32]))
+    G = int(r.choice([g for g in (1, 2, 4, 8) if E % g == 0]))
+    per = E // G
+    M = int(r.integers(1, G + 1))
+    n_top = int(r.integers(1, min(per, 16 // M) + 1))
+    T = int(r.integers(1, 301))
+    d = int(r.choice([128, 256, 384]))
+    f = int(r.choice([128, 256, 384]))
+    rho = float(r.choice([1.0, 2.5]))
+    return configs.MoEConfig(f"fuzz{seed}", T=T, d=d, E=E, G=G, M=M, k=M * n_top, f=f,
+                             route_scale=rho, bias="zero" if seed % 4 == 0 else "uniform",
+                             seed=31000 + seed)
+
+
 def run_layer(cfg, x, wg, b, W, dispatch=False, scales="fp32"):
     L = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.f, cfg.route_scale,
                      dispatch=dispatch, scales=scales)

@@ -19,7 +19,7 @@ from routing_fp8_grouped_amd import configs, inputs
 from oracle import backward as ob, fp8, quant as oq, permute as operm, layer as olayer
 from tests.gpu_util import (DEV, log, to_np, code_ambiguity, check_h_codes, gemm_noise,
                             block_max_products, MAXPROD_FACTOR, device_weights, OracleExperts,
-                            rel_l2_rows)
+                            rel_l2_rows, random_layer_config)
 from tests.test_gpu_kernels import bf16_tensor, gemm_case
 
 pytestmark = pytest.mark.gpu
@@ -371,15 +371,26 @@ def test_tiny_layer_backward():
     """The whole backward of the tiny layer, stage by stage, each against the
     backward oracle fed with the GPU's own inputs to that stage (so every
     check is bit-exact or within one GEMM's noise), then dX end to end."""
-    cfg = configs.get("tiny")
-    log(f"layer backward {cfg.name}")
+    check_layer_backward(configs.get("tiny"), 6)
+
+
+@pytest.mark.parametrize("seed", [0, 3, 5, 9, 17, 20])
+def test_layer_backward_random(seed):
+    """The same stage-by-stage backward checks on seeded random layers (T up
+    to 300, E 8-32, d and f 128-384; the forward on the weight-streaming or
+    the tiled GEMM)."""
+    check_layer_backward(random_layer_config(seed), 100 + seed)
+
+
+def check_layer_backward(cfg, dout_seed):
+    log(f"layer backward {cfg.name}: T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} G={cfg.G} M={cfg.M} k={cfg.k}")
     x, wg, b = inputs.host_inputs(cfg)
     bf16 = {}
     W = device_weights(cfg, bf16)
     Wt = W.transposed()
     L = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.f, cfg.route_scale)
     L.forward(x.to(DEV), wg.to(DEV), b.to(DEV), W, train=True)
-    rng = np.random.default_rng(6)
+    rng = np.random.default_rng(dout_seed)
     dout = bf16_tensor(rng.standard_normal((cfg.T, cfg.d)))
     dx, dw13, dw2, dgate = L.backward(dout.to(DEV), Wt)
     torch.cuda.synchronize()

@@ -33,7 +33,7 @@ from routing_fp8_grouped_amd import configs, inputs
 from oracle import route as oroute, permute as operm, layer as olayer
 from tests.gpu_util import (DEV, log, to_np, rel_l2_rows, device_weights, OracleExperts, run_layer,
                             layer_allowance, rows_within, check_h_codes, chain_report,
-                            stage_fed_tokens)
+                            stage_fed_tokens, random_layer_config)
 
 pytestmark = pytest.mark.gpu
 N_CASES = 24
@@ -121,24 +121,6 @@ def test_dispatch_chain_random(seed):
         f"{max(len(set((gi[t] // per).tolist())) for t in range(T))} of {M}")
 
 
-def draw_layer(seed):
-    """A whole-layer configuration: T in [1, 300], E in {8, 16, 32}, G | E,
-    M <= G, k = M * n <= min(M * E / G, 16), d and f in {128, 256, 384}."""
-    r = np.random.default_rng(9000 + seed)
-    E = int(r.choice([8, 16, 32]))
-    G = int(r.choice([g for g in (1, 2, 4, 8) if E % g == 0]))
-    per = E // G
-    M = int(r.integers(1, G + 1))
-    n_top = int(r.integers(1, min(per, 16 // M) + 1))
-    T = int(r.integers(1, 301))
-    d = int(r.choice([128, 256, 384]))
-    f = int(r.choice([128, 256, 384]))
-    rho = float(r.choice([1.0, 2.5]))
-    return configs.MoEConfig(f"fuzz{seed}", T=T, d=d, E=E, G=G, M=M, k=M * n_top, f=f,
-                             route_scale=rho, bias="zero" if seed % 4 == 0 else "uniform",
-                             seed=31000 + seed)
-
-
 def run_random_layer(cfg, rule):
     small = cfg.rows <= 16 * (cfg.E + 1)
     log(f"layer fuzz {cfg.name} ({rule} scales): T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} G={cfg.G} "
@@ -156,7 +138,7 @@ def run_random_layer(cfg, rule):
 
 @pytest.mark.parametrize("seed", range(N_LAYERS))
 def test_layer_random(seed):
-    cfg = draw_layer(seed)
+    cfg = random_layer_config(seed)
     L, ref, oe = run_random_layer(cfg, "fp32")
     r = ref["route"]
     ok = ~r["near_tie"]
@@ -187,7 +169,7 @@ def test_layer_random_pow2(seed):
     draws, against the oracle run with the power-of-two rule: routing and
     quantisation bit for bit, the stage-fed output within 5e-3 per row, the
     independent chain within its counted allowance."""
-    cfg = draw_layer(seed)
+    cfg = random_layer_config(seed)
     L, ref, oe = run_random_layer(cfg, "pow2")
     r = ref["route"]
     ok = ~r["near_tie"]
