@@ -287,6 +287,17 @@ def test_gemm_parity_random(seed):
     run_gemm_parity(counts, d, f, gather, 7 * seed + 1)
 
 
+@pytest.mark.parametrize("hi_rows,gather", [(41, True), (13, False)])
+def test_gemm_parity_max_groups(hi_rows, gather):
+    """The largest group count the GEMM entry points accept (1024): the tile
+    list's prefix over 16 chunks of 64 groups, about a fifth of the groups
+    empty.  Up to 40 rows per group (about 20 on average) takes the tiled
+    kernel, up to 12 the weight-streaming one."""
+    r = np.random.default_rng(4000 + hi_rows)
+    counts = [int(c) if r.random() > 0.2 else 0 for c in r.integers(1, hi_rows, 1024)]
+    run_gemm_parity(counts, 128, 128, gather, hi_rows)
+
+
 def run_gemm_parity(counts, d, f, gather, seed):
     log(f"grouped gemm counts={counts} d={d} f={f} gather={gather}")
     rng = np.random.default_rng(seed)
