@@ -152,6 +152,33 @@ def test_degenerate_layers(case):
     assert np.all(okr)
 
 
+@pytest.mark.parametrize("E,G,M,k", [(16, 4, 2, 4), (256, 8, 4, 8)])
+def test_zero_input_ties(E, G, M, k):
+    """All-zero activations with a zero bias: every logit is 0 and every
+    biased score exactly sigmoid(0) = 0.5, so all groups and all experts tie.
+    The tie rule (lower group index, then lower expert id) fixes the result:
+    groups 0 .. M-1 are kept and the top k over their experts (the count per
+    group is free) are the k lowest ids 0 .. k-1, every gate rho/k, codes and
+    scales of zero tiles (code 0, scale 1) for X and H, and a zero output.
+    E = 16 takes the general selection, E = 256 in 8 groups the V3 one."""
+    cfg = configs.MoEConfig(f"zeros{E}", T=70, d=256, E=E, G=G, M=M, k=k, f=128, bias="zero", seed=3)
+    log(f"zero input E={E} G={G} M={M} k={k}")
+    _, wg, b = inputs.host_inputs(cfg)
+    x = torch.zeros(cfg.T, cfg.d, dtype=torch.bfloat16)
+    W = device_weights(cfg)
+    L = run_layer(cfg, x, wg, b, W)
+    assert k <= M * (E // G)
+    want = np.arange(k, dtype=np.int32)
+    r = oroute.route(x.float().numpy(), wg.float().numpy(), b.numpy(), G, M, k, cfg.route_scale)
+    assert np.all(r["idx"] == want)                   # the oracle's tie rule
+    assert np.all(to_np(L.idx) == want)
+    assert np.all(to_np(L.w) == np.float32(cfg.route_scale / k))
+    assert not to_np(L.xq).any() and np.all(to_np(L.xs) == 1.0)
+    assert not to_np(L.h).any() and np.all(to_np(L.hs) == 1.0)
+    assert not to_np(L.y).view(np.uint16).any()
+    assert not to_np(L.out).view(np.uint16).any()
+
+
 FULL = ["decode_64", "prefill_4k", "uniform_16k", "zipf_16k"]
 
 
