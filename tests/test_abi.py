@@ -150,6 +150,10 @@ def test_gemm_validation(lib):
     assert call(h=None) == 1 and "h is NULL" in last(lib)
     assert call(h=MIS) == 1
     assert call(rows=0, h=None) == 0
+    # the kernels address rows and one expert's weights with 32-bit byte
+    # offsets: rows x max(d, f) and 2f x d must stay below 4 GiB
+    assert call(rows=599187, d=7168) == 2 and "4 GiB" in last(lib)
+    assert call(rows=100, d=65536, f=32768) == 2 and "4 GiB" in last(lib)
     # the two stages validate the same way
     up = lambda rows=100, d=256, h=A, row_src=A: lib.grouped_gemm_fp8_up(
         A, A, 10, row_src, A, 257, rows, d, 128, A, A, h, A, None)

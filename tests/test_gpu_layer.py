@@ -182,6 +182,51 @@ def test_zero_input_ties(E, G, M, k):
 FULL = ["decode_64", "prefill_4k", "uniform_16k", "zipf_16k"]
 
 
+def test_v3_max_tokens():
+    """65536 tokens at the V3 shape: 589824 grouped rows, whose FP8 rows and
+    BF16 outputs reach 98% of the 4 GiB the kernels' 32-bit byte offsets
+    address (the entry points refuse more).  Routing and quantisation on a
+    sample of 2048 tokens, the permutation's properties on all of them, and
+    the layer output of 64 tokens (among them the last four, whose rows lie
+    at the top of the offset range) stage-fed and on the independent chain."""
+    cfg = configs.with_tokens(configs.get("prefill_4k"), 65536, "prefill_64k")
+    assert 0.98 < cfg.rows * cfg.d / 2 ** 32 < 1.0
+    log(f"workload {cfg.name}: T={cfg.T} rows={cfg.rows}")
+    x, wg, b = inputs.host_inputs(cfg)
+    W = device_weights(cfg)
+    L = run_layer(cfg, x, wg, b, W)
+    log("  layer done on the GPU")
+    rng = np.random.default_rng(5)
+    rows = np.sort(np.concatenate([rng.choice(cfg.T - 4, 2044, replace=False), np.arange(cfg.T - 4, cfg.T)]))
+    xn = x[torch.from_numpy(rows)].float().numpy()
+    r = oroute.route(xn, wg.float().numpy(), b.numpy(), cfg.G, cfg.M, cfg.k, cfg.route_scale)
+    gi_all = to_np(L.idx)
+    gi = gi_all[rows]
+    ok = ~r["near_tie"]
+    assert np.array_equal(gi[ok], r["idx"][ok])
+    assert np.allclose(to_np(L.w)[rows][ok], r["w"][ok], rtol=2e-6)
+    rq, rs = oq.quant_1x128(xn)
+    assert np.array_equal(to_np(L.xq)[rows], rq) and np.array_equal(to_np(L.xs)[rows], rs)
+    check_permutation_properties(L, gi_all, cfg.T, cfg.k, cfg.E)
+    sample = np.sort(np.concatenate([rng.choice(cfg.T - 4, 60, replace=False), np.arange(cfg.T - 4, cfg.T)]))
+    oe = OracleExperts(cfg)
+    oe.prepare(sorted(set(gi_all[sample].reshape(-1).tolist()) | {cfg.E}))
+    sf = stage_fed_tokens(L, sample, oe, cfg.E)
+    err_sf = rel_l2_rows(to_np(L.out)[sample], sf)
+    log(f"  stage-fed out rel-L2 over {sample.size} tokens: max {err_sf.max():.2e}")
+    assert np.all(err_sf <= TOL), err_sf.max()
+    xs_ = x[torch.from_numpy(sample)].float().numpy()
+    rr = oroute.route(xs_, wg.float().numpy(), b.numpy(), cfg.G, cfg.M, cfg.k, cfg.route_scale)
+    okt = ~rr["near_tie"]
+    oe.prepare(sorted(set(rr["idx"][okt].reshape(-1).tolist())))
+    out, rs2, extra = olayer.moe_layer_tokens(xs_[okt], wg.float().numpy(), b.numpy(), oe, cfg.G, cfg.M,
+                                              cfg.k, cfg.route_scale)
+    allow = token_allowance(extra, rs2, oe, cfg.E)
+    okr, err, _ = rows_within(to_np(L.out)[sample[okt]], out, allow, TOL)
+    log(f"  {int(okt.sum())} tokens, " + chain_report(err, rows_within.allow_rel, TOL))
+    assert np.all(okr)
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_v3_workload(name):
     cfg = configs.get(name)
