@@ -182,6 +182,37 @@ def test_zero_input_ties(E, G, M, k):
 FULL = ["decode_64", "prefill_4k", "uniform_16k", "zipf_16k"]
 
 
+@pytest.mark.parametrize("T", [1, 17])
+def test_v3_few_tokens(T):
+    """The V3 shape with 1 and 17 tokens (the weight-streaming GEMMs with
+    one row per touched expert, and a ragged 16-row chunk): every token's
+    routing, quantisation, and output stage-fed and on the independent chain."""
+    cfg = configs.with_tokens(configs.get("decode_64"), T, f"v3_T{T}")
+    log(f"workload {cfg.name}")
+    x, wg, b = inputs.host_inputs(cfg)
+    W = device_weights(cfg)
+    L = run_layer(cfg, x, wg, b, W)
+    xn = x.float().numpy()
+    r = oroute.route(xn, wg.float().numpy(), b.numpy(), cfg.G, cfg.M, cfg.k, cfg.route_scale)
+    ok = ~r["near_tie"]
+    gi = to_np(L.idx)
+    assert np.array_equal(gi[ok], r["idx"][ok])
+    rq, rs = oq.quant_1x128(xn)
+    assert np.array_equal(to_np(L.xq), rq) and np.array_equal(to_np(L.xs), rs)
+    check_permutation_properties(L, gi, cfg.T, cfg.k, cfg.E)
+    oe = OracleExperts(cfg)
+    oe.prepare(sorted(set(gi.reshape(-1).tolist()) | set(r["idx"].reshape(-1).tolist()) | {cfg.E}))
+    sf = stage_fed_tokens(L, np.arange(T), oe, cfg.E)
+    err_sf = rel_l2_rows(to_np(L.out), sf)
+    assert np.all(err_sf <= TOL), err_sf.max()
+    out, rs2, extra = olayer.moe_layer_tokens(xn[ok], wg.float().numpy(), b.numpy(), oe, cfg.G, cfg.M,
+                                              cfg.k, cfg.route_scale)
+    allow = token_allowance(extra, rs2, oe, cfg.E)
+    okr, err, _ = rows_within(to_np(L.out)[ok], out, allow, TOL)
+    log(f"  stage-fed max {err_sf.max():.2e}; " + chain_report(err, rows_within.allow_rel, TOL))
+    assert np.all(okr)
+
+
 def test_v3_max_tokens():
     """65536 tokens at the V3 shape: 589824 grouped rows, whose FP8 rows and
     BF16 outputs reach 98% of the 4 GiB the kernels' 32-bit byte offsets
