@@ -27,6 +27,13 @@ class MoEConfig:
     zipf_s: float = 1.1
     seed: int = 20241227
     note: str = ""
+    weight_seed: int = 0    # seed of the expert weights; 0: the workload's own seed
+
+    @property
+    def expert_seed(self):
+        """Seed of the expert weights: the V3 workloads share one set, as the
+        batches of a deployed layer run through the same resident weights."""
+        return self.weight_seed or self.seed
 
     @property
     def rows(self):
@@ -38,7 +45,7 @@ class MoEConfig:
         return self.rows * 6 * self.d * self.f
 
 
-V3 = dict(d=7168, E=256, G=8, M=4, k=8, f=2048)
+V3 = dict(d=7168, E=256, G=8, M=4, k=8, f=2048, weight_seed=20241227)
 
 # The skew strength is fixed offline by tests/calibrate_zipf_skew.py (bisection so
 # that the busiest routed expert receives about 4000 of the 16384*8 assignments).

@@ -11,7 +11,9 @@ Recipe (per configuration, see ``configs.py``):
       a_e = r_e^-s - mean(r^-s) for a seeded permutation r of the ranks 1..E,
       added in float32 before the BF16 rounding
   * selection bias b [E]      : FP32 U(-0.05, 0.05), or zeros      numpy PCG64, host
-  * expert weights, per expert e = 0..E (E = shared), each from its own seed:
+  * expert weights, per expert e = 0..E (E = shared), each from its own seed
+    derived from the configuration's expert seed (one set shared by the V3
+    workloads, as the batches of a deployed layer share its resident weights):
       W13[e] [2f, d] = BF16(N(0, 1/d))  (rows [0, f) gate W1, [f, 2f) up W3)
       W2[e]  [d, f]  = BF16(N(0, 1/d))
     drawn with torch's generator on the device that will hold them (the GPU for
@@ -65,7 +67,7 @@ def selection_bias(cfg):
 def expert_weights(cfg, e, device="cpu"):
     """(W13[e] [2f, d], W2[e] [d, f]) BF16 on ``device``; e = E is the shared expert."""
     g = torch.Generator(device=device)
-    g.manual_seed(cfg.seed * 4096 + 17 + e)
+    g.manual_seed(cfg.expert_seed * 4096 + 17 + e)
     std = 1.0 / float(np.sqrt(cfg.d))
     w13 = (torch.randn(2 * cfg.f, cfg.d, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
     w2 = (torch.randn(cfg.d, cfg.f, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)

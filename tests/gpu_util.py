@@ -56,11 +56,32 @@ class OracleExperts:
     oracle from the same BF16 weights the GPU quantised (regenerated per expert
     with the same seed, copied to the host)."""
 
+    # quantised experts of the most recently used weight sets, keyed by
+    # (expert seed, d, f, rule) and shared by every test in the process, so
+    # the V3 workloads, which draw their experts from one seed, quantise each
+    # expert once; least recently used sets go first once the sets hold more
+    # than CACHE_BYTES (a whole V3 set is about 11 GB)
+    _sets = {}
+    CACHE_BYTES = 24 << 30
+
     def __init__(self, cfg, bf16_cache=None, rule="fp32"):
         self.cfg = cfg
-        self.cache = {}
         self.bf16 = bf16_cache
         self.rule = rule
+        self.key = (cfg.expert_seed, cfg.d, cfg.f, rule)
+        sets = OracleExperts._sets
+        sets[self.key] = sets.pop(self.key, {})     # most recently used last
+        self.cache = sets[self.key]
+
+    def _trim(self):
+        sets = OracleExperts._sets
+        size = lambda c: sum(a.nbytes for q in c.values() for a in q)
+        total = sum(size(c) for c in sets.values())
+        for k in list(sets):
+            if total <= OracleExperts.CACHE_BYTES:
+                break
+            if k != self.key:
+                total -= size(sets.pop(k))
 
     def _host(self, e):
         if self.bf16 is not None and e in self.bf16:
@@ -79,6 +100,7 @@ class OracleExperts:
             res = ex.map(lambda e: (e, olayer.quantize_expert(*host[e], self.rule)), ids)
             for e, q in res:
                 self.cache[e] = q
+        self._trim()
 
     def __call__(self, e):
         if int(e) not in self.cache:
