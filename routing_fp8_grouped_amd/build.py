@@ -68,5 +68,24 @@ def build(verbose=False, extra=()):
     return LIB
 
 
+def build_c_program(src, out):
+    """Compile a C program that calls the library through include/moe.h only
+    (a plain C compiler, HIP's runtime API for device memory), linked against
+    the in-tree libmoe.so."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler (gcc) found")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    rpath_lib = os.path.relpath(PKG, os.path.dirname(os.path.abspath(out)))
+    cmd = [cc, "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(rocm, "include"), src, "-o", out,
+           "-L", PKG, "-lmoe", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           f"-Wl,-rpath,$ORIGIN/{rpath_lib}", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C compile failed: {src}\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -2,6 +2,7 @@
 before touching a GPU (CPU only: nothing here launches a kernel)."""
 
 import ctypes
+import os
 import subprocess
 
 import pytest
@@ -271,3 +272,13 @@ def test_roof_validation(lib):
     assert lib.moe_roof_hbm_latency(A, 64, 64, 10, A, None) == 1 and "start" in last(lib)
     assert lib.moe_roof_hbm_latency(A, 64, 0, 0, A, None) == 1 and "steps" in last(lib)
     assert lib.moe_roof_hbm_latency(MIS4, 64, 0, 10, A, None) == 1 and "next" in last(lib)
+
+
+def test_header_is_c(tmp_path, lib):
+    """include/moe.h is a C header: a C11 program using every call of the
+    layer (tests/c_abi_layer.c) compiles with -Wall -Wextra -Werror and links
+    against libmoe.so (the GPU tier runs it)."""
+    from routing_fp8_grouped_amd import build as b
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_layer.c")
+    out = b.build_c_program(src, str(tmp_path / "c_abi_layer"))
+    assert os.path.getsize(out) > 0
