@@ -218,19 +218,30 @@ def test_tiny_layer_pow2_every_token():
     assert np.all(okr)
 
 
-def test_v3_pow2_sampled_tokens():
-    cfg = configs.get("prefill_4k")
+@pytest.mark.parametrize("name,T", [("prefill_4k", None), ("decode_64", 17)])
+def test_v3_pow2_sampled_tokens(name, T):
+    """The power-of-two variant at the V3 shape: 4096 tokens (the tiled GEMMs
+    on the hardware block-scaled MFMA, 64 sampled tokens, and a second run
+    equal byte for byte) and 17 tokens (the weight-streaming GEMMs with
+    power-of-two requantisation, every token)."""
+    cfg = configs.get(name) if T is None else configs.with_tokens(configs.get(name), T)
     log(f"pow2 workload {cfg.name}: T={cfg.T}")
     x, wg, b = inputs.host_inputs(cfg)
     W = device_weights(cfg, pow2=True)
     L = run_layer(cfg, x, wg, b, W, scales="pow2")
+    if T is None:
+        L2 = run_layer(cfg, x, wg, b, W, scales="pow2")
+        for nm in ("idx", "w", "xq", "xs", "offsets", "pos", "row_token", "h", "hs", "y", "out"):
+            assert torch.equal(getattr(L, nm), getattr(L2, nm)), nm
+        del L2
     xn = x.float().numpy()
     r = oroute.route(xn, wg.float().numpy(), b.numpy(), cfg.G, cfg.M, cfg.k, cfg.route_scale)
     ok = ~r["near_tie"]
     assert np.array_equal(to_np(L.idx)[ok], r["idx"][ok])
     rq, rs = oq.quant_1x128(xn, "pow2")
     assert np.array_equal(to_np(L.xq), rq) and np.array_equal(to_np(L.xs), rs)
-    sample = np.sort(np.random.default_rng(4).choice(np.nonzero(ok)[0], 64, replace=False))
+    sample = (np.nonzero(ok)[0] if cfg.T <= 64 else
+              np.sort(np.random.default_rng(4).choice(np.nonzero(ok)[0], 64, replace=False)))
     oe = OracleExperts(cfg, rule="pow2")
     oe.prepare(sorted(set(r["idx"][sample].reshape(-1).tolist()) | {cfg.E}))
     sf = stage_fed_tokens(L, sample, oe, cfg.E)
