@@ -364,6 +364,12 @@ class MoEWeights:
         return t
 
 
+# From this many tokens the layer quantises X on a side stream beside the
+# router (measured: 0.05 ms less per step at 16384 tokens; at 64 tokens the
+# fork and join cost more than the overlap gains).
+OVERLAP_QUANT_T = 2048
+
+
 class MoELayer:
     """Buffers and call sequence of the layer for up to ``T`` tokens:
     moe_route -> fp8_quant_1x128 -> moe_permute -> grouped_gemm_fp8_swiglu -> moe_combine.
@@ -374,7 +380,12 @@ class MoELayer:
 
     ``scales="pow2"`` runs the power-of-two scale variant: X and H get
     power-of-two scales and the GEMMs use the hardware block-scaled MFMA (the
-    weights must then be quantised with ``pow2=True``)."""
+    weights must then be quantised with ``pow2=True``).
+
+    From OVERLAP_QUANT_T tokens on, the activation quantisation runs on a
+    side stream of the layer's own (default priority), forked from and joined
+    back into the caller's stream within ``forward``, so the calls stay
+    ordered on that stream as seen by the caller (and capturable in a graph)."""
 
     def __init__(self, T, d, E, n_groups, topk_groups, topk, f, route_scale=2.5, device="cuda",
                  dispatch=False, scales="fp32"):
@@ -384,6 +395,7 @@ class MoELayer:
         self.T, self.d, self.E, self.k, self.f = T, d, E, topk, f
         self.n_groups, self.topk_groups, self.route_scale = n_groups, topk_groups, route_scale
         self.dispatch = dispatch
+        self._side = None        # stream of the overlapped activation quantisation
         rows = T * topk + T
         dev = dict(device=device)
         self.idx = torch.empty(T, topk, dtype=torch.int32, **dev)
@@ -408,11 +420,29 @@ class MoELayer:
         ``train`` the first expert GEMM also caches [G, U] in FP8 for
         ``backward`` (FP32-scale method only)."""
         mark = mark or (lambda name: None)
-        moe_route(x, wg, bias, self.n_groups, self.topk_groups, self.k, self.route_scale,
-                  self.idx, self.w, stream, workspace=self.route_ws)
-        mark("route")
-        (fp8_quant_1x128_pow2 if self.pow2 else fp8_quant_1x128)(x, self.xq, self.xs, stream)
-        mark("quant")
+        quant = fp8_quant_1x128_pow2 if self.pow2 else fp8_quant_1x128
+        if self.T >= OVERLAP_QUANT_T:
+            # the activation quantisation does not depend on the routing: on a
+            # side stream it runs beside the router (whose workgroups leave
+            # room on every CU), joined before the expert GEMMs.  The side
+            # stream first waits for everything before this call on the
+            # caller's stream (x, and the previous step's reads of xq/xs).
+            main = torch.cuda.current_stream() if stream is None else stream
+            if self._side is None:
+                self._side = torch.cuda.Stream(device=x.device)
+            self._side.wait_stream(main)
+            quant(x, self.xq, self.xs, self._side)
+            moe_route(x, wg, bias, self.n_groups, self.topk_groups, self.k, self.route_scale,
+                      self.idx, self.w, main, workspace=self.route_ws)
+            mark("route")
+            main.wait_stream(self._side)
+            mark("quant")
+        else:
+            moe_route(x, wg, bias, self.n_groups, self.topk_groups, self.k, self.route_scale,
+                      self.idx, self.w, stream, workspace=self.route_ws)
+            mark("route")
+            quant(x, self.xq, self.xs, stream)
+            mark("quant")
         if self.dispatch:
             moe_permute(self.idx, self.E, self.offsets, self.pos, self.row_token, self.ws,
                         self.xq, self.xs, self.xq_perm, self.xs_perm, stream)

@@ -2,8 +2,10 @@
 and replayed: every replay, with eager work of another layer in between and
 with new input data written into the captured input buffer, gives the eager
 result bit for bit.  The library allocates nothing and issues no memsets, so
-its launches are capture-safe; this checks it on the tiled GEMM path (tiny)
-and on the weight-streaming path with the two-kernel router (decode_64)."""
+its launches are capture-safe; this checks it on the tiled GEMM path (tiny),
+on the weight-streaming path with the two-kernel router (decode_64), and with
+the activation quantisation forked onto the layer's side stream (2048 tokens
+and up)."""
 
 import pytest
 import torch
@@ -25,9 +27,14 @@ def _layer(cfg):
     return moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.G, cfg.M, cfg.k, cfg.f, cfg.route_scale)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_64"])
+CASES = {"tiny": configs.get("tiny"), "decode_64": configs.get("decode_64"),
+         "side_stream": configs.MoEConfig("side_stream", T=moe.OVERLAP_QUANT_T, d=256, E=16, G=4, M=2, k=4,
+                                          f=128, seed=9)}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
 def test_forward_replays_in_a_graph(name):
-    cfg = configs.get(name)
+    cfg = CASES[name]
     log(f"graph capture of the {name} forward")
     x, wg, b = inputs.host_inputs(cfg)
     W = device_weights(cfg)
